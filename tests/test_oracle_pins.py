@@ -1,0 +1,408 @@
+"""Pins of the CPU float64 oracle to facts outside itself.
+
+Each test checks the oracle against something the pages or the mathematics
+fix: hand-worked values (tests/golden/hand_cases.json), closed forms,
+invariants, special cases that reduce to something simpler, and brute force
+over explicit index loops on tiny inputs.  The shapes are deliberately
+non-square (H != nq*hd, I != H) so a transposed weight fails on shape.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+MATH_NS = {"sqrt": math.sqrt, "cos": math.cos, "sin": math.sin, "exp": math.exp}
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _eval(exprs):
+    return np.array([eval(e, {"__builtins__": {}}, MATH_NS) for e in exprs], dtype=np.float64)
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+@pytest.mark.parametrize("case", _golden()["rmsnorm"])
+def test_rmsnorm_hand_cases(case):
+    got = oracle.rms_norm(np.array(case["x"]), np.array(case["gain"]), case["eps"])
+    np.testing.assert_allclose(got, _eval(case["expected"]), rtol=1e-15, atol=1e-15)
+
+
+def test_rmsnorm_output_rms_closed_form():
+    # unit gain: rms(out) = sqrt(ms / (ms + eps)) for every row
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((7, 33)) * 0.7
+    eps = 0.3
+    out = oracle.rms_norm(x, np.ones(33), eps)
+    ms = np.mean(x * x, axis=1)
+    np.testing.assert_allclose(np.sqrt(np.mean(out * out, axis=1)), np.sqrt(ms / (ms + eps)),
+                               rtol=1e-14)
+
+
+def test_rmsnorm_scale_invariant_at_zero_eps():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 40))
+    g = 1 + 0.05 * rng.standard_normal(40)
+    np.testing.assert_allclose(oracle.rms_norm(7.5 * x, g, 0.0), oracle.rms_norm(x, g, 0.0),
+                               rtol=1e-14)
+
+
+# ---------------------------------------------------------------- RoPE
+
+@pytest.mark.parametrize("case", _golden()["rope"])
+def test_rope_hand_cases(case):
+    x = np.array(case["x"], dtype=np.float64)[None, None, :]
+    got = oracle.apply_rope(x, np.array([case["position"]]), case["theta"])[0, 0]
+    np.testing.assert_allclose(got, _eval(case["expected"]), rtol=1e-15, atol=1e-15)
+
+
+def test_rope_position_zero_is_identity_bitwise():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((3, 5, 64))
+    out = oracle.apply_rope(x, np.zeros(3, dtype=np.int64), 5e5)
+    assert np.array_equal(out, x)
+
+
+def test_rope_preserves_pair_and_head_norms():
+    rng = np.random.default_rng(3)
+    hd = 128
+    x = rng.standard_normal((9, 4, hd))
+    pos = np.array([0, 1, 7, 100, 511, 4095, 30720, 32767, 12345])
+    out = oracle.apply_rope(x, pos, 5e5)
+    h = hd // 2
+    np.testing.assert_allclose(out[..., :h] ** 2 + out[..., h:] ** 2,
+                               x[..., :h] ** 2 + x[..., h:] ** 2, rtol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(out, axis=-1), np.linalg.norm(x, axis=-1),
+                               rtol=1e-13)
+
+
+def test_rope_depends_on_relative_position_only():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 1, 64))
+    k = rng.standard_normal((1, 1, 64))
+
+    def dot(p, pk):
+        return float(np.sum(oracle.apply_rope(q, np.array([p]), 1e4) *
+                            oracle.apply_rope(k, np.array([pk]), 1e4)))
+
+    for p, pk, d in [(5, 2, 11), (100, 0, 300), (17, 17, 1000)]:
+        assert dot(p, pk) == pytest.approx(dot(p + d, pk + d), rel=1e-10, abs=1e-12)
+
+
+# ---------------------------------------------------------------- SiLU / SwiGLU
+
+def test_silu_hand_cases():
+    case = _golden()["silu"][0]
+    np.testing.assert_allclose(oracle.silu(np.array(case["z"])), _eval(case["expected"]),
+                               rtol=1e-15, atol=0)
+
+
+def test_silu_limits():
+    assert oracle.silu(np.array([40.0]))[0] == pytest.approx(40.0, rel=1e-15)
+    assert abs(oracle.silu(np.array([-40.0]))[0]) < 1e-15
+
+
+# ---------------------------------------------------------------- 1-bit decode
+
+def test_sign1_hand_case():
+    case = _golden()["sign1"][0]
+    bits = np.array([case["words"]], dtype=np.uint32)
+    scales = np.array([[case["scale"]]], dtype=np.float64)
+    w = oracle.decode_sign1(bits, scales)[0]
+    expect = np.full(128, -case["scale"])
+    expect[case["plus_columns"]] = case["scale"]
+    assert np.array_equal(w, expect)
+
+
+def test_sign1_all_ones_gives_scaled_group_sums():
+    # every bit set: W[o][k] = s[o][k // 128], so Y[t][o] = sum_g s[o][g] * sum_{k in g} X[t][k]
+    rng = np.random.default_rng(5)
+    n, k = 6, 384
+    bits = np.full((n, k // 32), 0xFFFFFFFF, dtype=np.uint32)
+    scales = np.abs(rng.standard_normal((n, k // 128)))
+    x = rng.standard_normal((4, k))
+    y = x @ oracle.decode_sign1(bits, scales).T
+    group_sums = x.reshape(4, 3, 128).sum(axis=2)          # [t, g]
+    np.testing.assert_allclose(y, group_sums @ scales.T, rtol=1e-12)
+
+
+def test_sign1_negating_all_bits_negates_weights():
+    rng = np.random.default_rng(6)
+    bits = rng.integers(0, 1 << 32, size=(5, 8), dtype=np.uint32)
+    scales = np.abs(rng.standard_normal((5, 2)))
+    assert np.array_equal(oracle.decode_sign1(~bits, scales), -oracle.decode_sign1(bits, scales))
+
+
+# ---------------------------------------------------------------- attention
+
+def _brute_attention(q, kc, vc, positions):
+    """Explicit index loops: per query row, head and key."""
+    r, nq, hd = q.shape
+    nkv = kc.shape[0]
+    out = np.zeros((r, nq, hd))
+    for i in range(r):
+        for h in range(nq):
+            j = h * nkv // nq
+            s = [sum(q[i, h, d] * kc[j, u, d] for d in range(hd)) / math.sqrt(hd)
+                 for u in range(positions[i] + 1)]
+            m = max(s)
+            e = [math.exp(v - m) for v in s]
+            tot = sum(e)
+            for d in range(hd):
+                out[i, h, d] = sum(e[u] * vc[j, u, d] for u in range(len(e))) / tot
+    return out
+
+
+def test_attention_matches_brute_force():
+    rng = np.random.default_rng(7)
+    nq, nkv, hd, S = 6, 2, 8, 12
+    q = rng.standard_normal((5, nq, hd))
+    kc = rng.standard_normal((nkv, S, hd))
+    vc = rng.standard_normal((nkv, S, hd))
+    pos = np.array([0, 3, 4, 9, 11])
+    np.testing.assert_allclose(oracle.causal_gqa_attention(q, kc, vc, pos),
+                               _brute_attention(q, kc, vc, pos), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_first_token_returns_v0():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 4, 16))
+    kc = rng.standard_normal((2, 5, 16))
+    vc = rng.standard_normal((2, 5, 16))
+    out = oracle.causal_gqa_attention(q, kc, vc, np.array([0]))
+    assert np.array_equal(out[0, :2], np.broadcast_to(vc[0, 0], (2, 16)))
+    assert np.array_equal(out[0, 2:], np.broadcast_to(vc[1, 0], (2, 16)))
+
+
+def test_attention_equal_keys_gives_mean_of_visible_values():
+    rng = np.random.default_rng(9)
+    kc = np.broadcast_to(rng.standard_normal(16), (1, 10, 16)).copy()
+    vc = rng.standard_normal((1, 10, 16))
+    q = rng.standard_normal((3, 2, 16))
+    pos = np.array([2, 5, 9])
+    out = oracle.causal_gqa_attention(q, kc, vc, pos)
+    for i, p in enumerate(pos):
+        np.testing.assert_allclose(out[i, 0], vc[0, :p + 1].mean(axis=0), rtol=1e-13)
+
+
+def test_attention_gqa_head_mapping():
+    # kv head j holds the constant value j: query head h must read kv head h // (nq/nkv)
+    nq, nkv, hd = 8, 4, 4
+    rng = np.random.default_rng(10)
+    vc = np.zeros((nkv, 6, hd)) + np.arange(nkv)[:, None, None]
+    kc = rng.standard_normal((nkv, 6, hd))
+    q = rng.standard_normal((2, nq, hd))
+    out = oracle.causal_gqa_attention(q, kc, vc, np.array([3, 5]))
+    for h in range(nq):
+        np.testing.assert_allclose(out[:, h], h // 2, atol=1e-14)
+
+
+def test_attention_mha_when_nq_equals_nkv():
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((3, 3, 8))
+    kc = rng.standard_normal((3, 7, 8))
+    vc = rng.standard_normal((3, 7, 8))
+    pos = np.array([1, 4, 6])
+    out = oracle.causal_gqa_attention(q, kc, vc, pos)
+    for h in range(3):
+        np.testing.assert_allclose(out[:, h:h + 1],
+                                   oracle.causal_gqa_attention(q[:, h:h + 1], kc[h:h + 1],
+                                                               vc[h:h + 1], pos)[:, 0:1],
+                                   rtol=1e-14)
+
+
+# ---------------------------------------------------------------- the layer
+
+TINY = synth.Shape("pin", hidden=96, inter=40, nq=4, nkv=2, head_dim=16, qk_norm=True,
+                   eps=1e-6, theta=1e4, n_tokens=9, start=0, max_seq=32, n_layers=2,
+                   dtype="f32", seed=77)
+
+
+def _tiny_weights(shape):
+    return [synth.widen_layer(shape, synth.layer_weights(shape, l)) for l in range(shape.n_layers)]
+
+
+def _nan_caches(shape):
+    c = np.full((shape.n_layers, shape.nkv, shape.max_seq, shape.head_dim), np.nan)
+    return c, c.copy()
+
+
+def test_layer_zero_output_projections_pass_residual_through():
+    ws = _tiny_weights(TINY)[0]
+    ws["w_o"] = np.zeros_like(ws["w_o"])
+    ws["w_down"] = np.zeros_like(ws["w_down"])
+    x = np.random.default_rng(12).standard_normal((5, TINY.hidden))
+    kc, vc = _nan_caches(TINY)
+    assert np.array_equal(oracle.prefill_layer(TINY, ws, 0, x, 0, kc, vc), x)
+
+
+def test_layer_writes_exactly_the_slots_of_its_tokens():
+    ws = _tiny_weights(TINY)
+    kc, vc = _nan_caches(TINY)
+    x = np.random.default_rng(13).standard_normal((6, TINY.hidden))
+    kc[:, :, :4] = 0.25
+    vc[:, :, :4] = -0.5
+    oracle.prefill_layer(TINY, ws[1], 1, x, 4, kc, vc)
+    written = ~np.isnan(kc)
+    expect = np.zeros_like(written)
+    expect[:, :, :4] = True
+    expect[1, :, 4:10] = True
+    assert np.array_equal(written, expect)
+    assert np.array_equal(~np.isnan(vc), expect)
+    assert np.all(kc[0, :, :4] == 0.25)
+
+
+def test_layer_k_slot_holds_key_roped_at_its_absolute_position():
+    # constant hidden rows, unit gains, eps 0: xn is the all-ones row; W_k row 0 of
+    # kv head j is 1/H, every other K row 0, so the pre-RoPE key is e_0 and the
+    # roped key at absolute position p is cos(p) on element 0, sin(p) on hd/2.
+    sh = TINY.replace(qk_norm=False, eps=0.0)
+    ws = _tiny_weights(sh)[0]
+    ws["attn_norm"] = np.ones(sh.hidden)
+    wqkv = ws["w_qkv"].copy()
+    k0 = sh.nq * sh.head_dim
+    wqkv[k0:k0 + sh.nkv * sh.head_dim] = 0.0
+    for j in range(sh.nkv):
+        wqkv[k0 + j * sh.head_dim] = 1.0 / sh.hidden
+    ws["w_qkv"] = wqkv
+    kc, vc = _nan_caches(sh)
+    start, n = 11, 5
+    kc[:, :, :start] = 0.0
+    vc[:, :, :start] = 0.0
+    oracle.prefill_layer(sh, ws, 0, np.full((n, sh.hidden), 2.0), start, kc, vc)
+    for t in range(n):
+        p = start + t
+        expect = np.zeros(sh.head_dim)
+        expect[0], expect[sh.head_dim // 2] = math.cos(p), math.sin(p)
+        for j in range(sh.nkv):
+            np.testing.assert_allclose(kc[0, j, p], expect, atol=1e-15)
+
+
+def test_layer_value_path_running_mean():
+    # Q = K = 0 makes every score 0, so attention is the plain mean of the visible
+    # values; V head j is xn itself on its first hd dims; W_o copies head 0 back
+    # onto hidden dims [0, hd); W_down = 0.  Token t at start 0 must then gain the
+    # mean of xn[0..t] on those dims: this pins the V slice, the causal window,
+    # the cache round trip and the residual add.  QK-norm is on (a zero row
+    # normalises to zero), so a V that were normed as well would show here.
+    sh = TINY
+    ws = _tiny_weights(sh)[0]
+    hd, nq, nkv, H = sh.head_dim, sh.nq, sh.nkv, sh.hidden
+    wqkv = np.zeros((sh.qkv_dim, H))
+    for j in range(nkv):
+        for d in range(hd):
+            wqkv[(nq + nkv) * hd + j * hd + d, d] = 1.0
+    ws["w_qkv"] = wqkv
+    wo = np.zeros((H, nq * hd))
+    wo[np.arange(hd), np.arange(hd)] = 1.0
+    ws["w_o"] = wo
+    ws["w_down"] = np.zeros_like(ws["w_down"])
+    x = np.random.default_rng(14).standard_normal((7, H))
+    kc, vc = _nan_caches(sh)
+    out = oracle.prefill_layer(sh, ws, 0, x, 0, kc, vc)
+    xn = oracle.rms_norm(x, ws["attn_norm"], sh.eps)
+    for t in range(7):
+        expect = x[t].copy()
+        expect[:hd] += xn[:t + 1, :hd].mean(axis=0)
+        np.testing.assert_allclose(out[t], expect, rtol=1e-13, atol=1e-13)
+
+
+def test_layer_ffn_gate_and_up_halves():
+    # W_o = 0 and a unit W_down row map; gate row i reads xn2 dim 0, up row i reads
+    # dim 1: the FFN adds silu(xn2[0]) * xn2[1] to hidden dim i for i < I.
+    sh = TINY
+    ws = _tiny_weights(sh)[0]
+    H, I = sh.hidden, sh.inter
+    ws["w_o"] = np.zeros_like(ws["w_o"])
+    wgu = np.zeros((2 * I, H))
+    wgu[:I, 0] = 1.0
+    wgu[I:, 1] = 1.0
+    ws["w_gate_up"] = wgu
+    wd = np.zeros((H, I))
+    wd[np.arange(I), np.arange(I)] = 1.0
+    ws["w_down"] = wd
+    x = np.random.default_rng(15).standard_normal((3, H))
+    kc, vc = _nan_caches(sh)
+    out = oracle.prefill_layer(sh, ws, 0, x, 0, kc, vc)
+    xn2 = oracle.rms_norm(x, ws["ffn_norm"], sh.eps)
+    add = xn2[:, 0] / (1 + np.exp(-xn2[:, 0])) * xn2[:, 1]
+    expect = x.copy()
+    expect[:, :I] += add[:, None]
+    np.testing.assert_allclose(out, expect, rtol=1e-13, atol=1e-14)
+
+
+def _run_chunked(shape, ws, x, start, mb, prefill=None):
+    kc, vc = _nan_caches(shape)
+    if prefill is not None:
+        kc[:, :, :start], vc[:, :, :start] = prefill
+    out, _ = oracle.prefill_chunk(shape, ws, x, start, mb, kc, vc)
+    return out, kc, vc
+
+
+def test_one_shot_chunked_and_token_by_token_agree():
+    ws = _tiny_weights(TINY)
+    rng = np.random.default_rng(16)
+    start, n = 3, 9
+    pre = (rng.standard_normal((2, 2, start, 16)), rng.standard_normal((2, 2, start, 16)))
+    x = rng.standard_normal((n, TINY.hidden))
+    one, k1, v1 = _run_chunked(TINY, ws, x, start, 0, pre)
+    for mb in (1, 2, 4, 5):
+        got, k2, v2 = _run_chunked(TINY, ws, x, start, mb, pre)
+        np.testing.assert_allclose(got, one, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(k2, k1, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(v2, v1, rtol=1e-12, atol=1e-12)
+        assert np.array_equal(np.isnan(k2), np.isnan(k1))
+
+
+def test_row_sampling_matches_full_layer():
+    ws = _tiny_weights(TINY)[0]
+    x = np.random.default_rng(17).standard_normal((8, TINY.hidden))
+    kc, vc = _nan_caches(TINY)
+    full = oracle.prefill_layer(TINY, ws, 0, x, 0, kc, vc)
+    kc, vc = _nan_caches(TINY)
+    rows = np.array([0, 5, 7])
+    part = oracle.prefill_layer(TINY, ws, 0, x, 0, kc, vc, rows=rows)
+    np.testing.assert_allclose(part, full[rows], rtol=1e-13, atol=1e-14)
+
+
+def test_head_reads_last_row_normed():
+    sh = TINY
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((4, sh.hidden))
+    g = 1 + 0.05 * rng.standard_normal(sh.hidden)
+    logits = oracle.lm_head_logits(x[-1], g, 1e-5, np.eye(sh.hidden))
+    ms = np.mean(x[-1] ** 2)
+    np.testing.assert_allclose(logits, g * x[-1] / math.sqrt(ms + 1e-5), rtol=1e-14)
+
+
+def test_sign1_layer_equals_dense_layer_of_decoded_weights():
+    sh = TINY.replace(hidden=128, inter=256, nq=2, nkv=1, head_dim=64, wformat="sign1")
+    w_q = synth.widen_layer(sh, synth.layer_weights(sh, 0))
+    w_d = {k: (oracle.decode_sign1(*v) if isinstance(v, tuple) else v) for k, v in w_q.items()}
+    x = np.random.default_rng(19).standard_normal((3, sh.hidden))
+    kc, vc = _nan_caches(sh)
+    a = oracle.prefill_layer(sh, w_q, 0, x, 0, kc, vc)
+    kc, vc = _nan_caches(sh)
+    b = oracle.prefill_layer(sh, w_d, 0, x, 0, kc, vc)
+    assert np.array_equal(a, b)
+
+
+def test_chunk_head_runs_on_final_token_of_last_micro_batch():
+    sh = TINY
+    ws = _tiny_weights(sh)
+    x = np.random.default_rng(20).standard_normal((7, sh.hidden))
+    g = np.ones(sh.hidden)
+    kc, vc = _nan_caches(sh)
+    out, logits = oracle.prefill_chunk(sh, ws, x, 0, 3, kc, vc, final_gain=g,
+                                       head=np.eye(sh.hidden), final_eps=0.0)
+    last = out[-1]
+    np.testing.assert_allclose(logits, last / math.sqrt(np.mean(last ** 2)), rtol=1e-14)
