@@ -1,0 +1,191 @@
+"""Prefill throughput of one Llama-3-8B-shape decoder layer on one MI355X.
+
+A step is one tlp_prefill_layer call (the whole layer: RMSNorm, QKV GEMM,
+QK-norm/RoPE/KV store, causal GQA attention, O GEMM + residual, FFN norm,
+gate/up GEMM + SwiGLU, down GEMM + residual) over a 512-token micro-batch at
+start position 0: hidden 4096, intermediate 14336, 32 q / 8 kv heads,
+head_dim 128, bf16 weights N(0, 0.02) and inputs N(0, 1), fp32 accumulation.
+Every step reads its own copy of the input rows (prepared before the timed
+region), so every step does identical work; repeated calls at one start
+position rewrite the same cache slots.
+
+Prints one JSON line: tokens/s per layer, per-kernel HIP-event times from the
+library's profiler, the roofline of the dominant kernel (the gate/up GEMM) and
+the CPU float64 oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "prefill tokens/sec per layer + achieved MFMA TFLOP/s fraction, 8B shape"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def layer_flops(sh, n, start):
+    """Algorithmic flops of one layer call: projections and causal attention."""
+    H, I, hd, nq, nkv = sh.hidden, sh.inter, sh.head_dim, sh.nq, sh.nkv
+    gemm = {
+        "qkv_gemm": 2 * n * H * (nq + 2 * nkv) * hd,
+        "o_gemm": 2 * n * nq * hd * H,
+        "gate_up_gemm": 2 * n * H * 2 * I,
+        "down_gemm": 2 * n * I * H,
+    }
+    keys = n * start + n * (n + 1) // 2
+    return gemm, 4 * hd * nq * keys
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(sh, w, x, kc, vc, budget_s=20.0):
+    """The float64 oracle on the host cores: whole layer calls, same inputs."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    w64 = synth.widen_layer(sh, w)
+    x64 = synth.widen(x, sh.dtype)
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        kc64, vc64 = synth.widen(kc, sh.dtype), synth.widen(vc, sh.dtype)
+        t0 = time.perf_counter()
+        oracle.prefill_layer(sh, w64, 0, x64, sh.start, kc64, vc64)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all > budget_s / 2 or len(times) >= 5:
+            break
+    t = float(np.mean(times))
+    return {"value": sh.n_tokens / t, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{len(times)} full float64 oracle layer call(s) of the same workload "
+                      f"({sh.n_tokens} tokens at start {sh.start}), mean {t:.3f} s each"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3-8b-layer",
+                    choices=["llama3-8b-layer", "qwen3-8b-sign1-layer", "llama3-8b-long-ctx"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design in DESIGN.md, not a measured run",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_layer_prefill_amd as tlp
+    from transformer_layer_prefill_amd import tensors
+
+    sh = synth.WORKLOADS[args.workload]
+    log(f"[bench] generating {sh.name}")
+    w = synth.layer_weights(sh, 0)
+    x = synth.hidden_input(sh)
+    kc, vc = synth.kv_caches(sh)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = tensors.config_of(sh)
+    dl = tensors.DeviceLayer(w, dev)
+    kcd, vcd = tensors.to_device(kc, dev), tensors.to_device(vc, dev)
+    cos, sin = tlp.rope_table(sh.theta, sh.head_dim, sh.max_seq)
+    cosd, sind = tensors.to_device(cos, dev), tensors.to_device(sin, dev)
+    x0 = tensors.to_device(x, dev)
+    ws = torch.empty(tlp.workspace_bytes(cfg, sh.n_tokens), dtype=torch.uint8, device=dev)
+    n_buf = args.warmup + args.steps
+    hiddens = [x0.clone() for _ in range(n_buf)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        tlp.prefill_layer(cfg, dl.struct, 0, hiddens[i], sh.n_tokens, sh.start, kcd, vcd, cosd,
+                          sind, ws, stream=stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps bracketed by synchronisation; HIP events from the
+    # library's profiler time every kernel on the stream it runs on
+    log(f"[bench] timing {args.steps} steps")
+    tlp.profile_begin()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = tlp.profile_end()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    value = sh.n_tokens / (ms_step * 1e-3)
+
+    gemm_flops, attn_flops = layer_flops(sh, sh.n_tokens, sh.start)
+    kernels = {}
+    for k, (n, ms) in prof.items():
+        if n:
+            kernels[k] = {"launches": n, "avg_us": 1e3 * ms / n}
+    gemm_us = sum(kernels[k]["avg_us"] for k in gemm_flops)
+    proj_tflops = sum(gemm_flops.values()) / (gemm_us * 1e-6) / 1e12
+    attn_us = kernels["attention"]["avg_us"]
+    attn_tflops = attn_flops / (attn_us * 1e-6) / 1e12
+    for k, f in gemm_flops.items():
+        kernels[k]["tflops"] = f / (kernels[k]["avg_us"] * 1e-6) / 1e12
+    kernels["attention"]["tflops"] = attn_tflops
+
+    dom = "gate_up_gemm"
+    dom_us = kernels[dom]["avg_us"]
+    achieved = gemm_flops[dom] / (dom_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_us": round(dom_us, 2), "flops_per_launch": gemm_flops[dom]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (float64 oracle on the host cores)")
+        cpu = cpu_baseline(sh, w, x, kc, vc)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": sh.name, "tokens": sh.n_tokens, "start_position": sh.start,
+                   "hidden": sh.hidden, "intermediate": sh.inter, "q_heads": sh.nq,
+                   "kv_heads": sh.nkv, "head_dim": sh.head_dim, "weights": sh.wformat,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "mfma_frac": {"projections": round(proj_tflops / PEAK_BF16_TFLOPS, 4),
+                      "attention": round(attn_tflops / PEAK_BF16_TFLOPS, 4)},
+        "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv
+                        for kk, vv in v.items()} for k, v in kernels.items()},
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * tlp.h - C ABI of the MI355X (gfx950) transformer-layer prefill library.
+ *
+ * The library runs the batched prefill forward of a dense Llama/Qwen3-style
+ * decoder layer over a micro-batch of prompt tokens, and a chunk driver that
+ * repeats it over every layer and micro-batch and finishes with a last-token
+ * LM head.  The operations are those of:
+ *   - oxibonsai-kernels 0.1.1, gpu_backend/metal_prefill.rs:
+ *     encode_layer_prefill steps 1-7 (the layer) and the "Tail" block of
+ *     encode_full_forward_prefill (final norm + LM head of the last token);
+ *   - oxibonsai-kernels 0.1.0, gpu_backend/metal_full_layer.rs: GpuKvCache
+ *     (cache layout [n_layers][n_kv][max_seq][head_dim]) and the fused
+ *     gate ++ up weight;
+ *   - turbospark-runtime 0.3.0, families/llama/prefill.rs:
+ *     prefill_chunk_real_llama_dense (micro-batches at start_position +
+ *     offset, head on the last micro-batch only).
+ *
+ * Conventions for every entry point:
+ *   - Every array argument is a DEVICE pointer unless marked "host".  The
+ *     caller owns every buffer; the library allocates nothing and keeps no
+ *     state between calls.
+ *   - Matrices are row-major.  Activations are token-major: row t of
+ *     hidden [n_tokens][hidden] is token t, at absolute position
+ *     start_position + t.  Projection weights are [out_features][in_features].
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     runs asynchronously; the caller synchronises.
+ *   - Arguments are validated before anything is enqueued.  On an error the
+ *     call returns a non-zero tlp_status, enqueues nothing and touches no
+ *     buffer; tlp_last_error() then describes it (thread-local text).  A
+ *     failed kernel launch returns TLP_ERR_HIP after earlier launches of the
+ *     same call may already be enqueued.
+ *   - Concurrent calls that share a workspace or a cache slot race; calls on
+ *     one stream are ordered.
+ */
+#ifndef TLP_H
+#define TLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TLP_OK = 0,
+  TLP_ERR_NULL = 1,        /* a required pointer is NULL */
+  TLP_ERR_SHAPE = 2,       /* a size or a shape relation is invalid */
+  TLP_ERR_POSITION = 3,    /* start_position < 0 or start_position + n_tokens > max_seq */
+  TLP_ERR_UNSUPPORTED = 4, /* a valid but unsupported combination (dtype, format, group size) */
+  TLP_ERR_WORKSPACE = 5,   /* workspace_bytes below tlp_workspace_bytes() */
+  TLP_ERR_HIP = 6          /* a HIP launch failed; tlp_last_error() has its text */
+} tlp_status;
+
+/* Activation / norm-gain / KV-cache element type. */
+typedef enum { TLP_F32 = 0, TLP_BF16 = 1 } tlp_dtype;
+
+/* Projection weight format.
+ * TLP_W_DENSE: [N][K] in the config's dtype.
+ * TLP_W_SIGN1_G128: 1-bit signs plus one fp16 scale per 128 consecutive
+ *   weights of a row (the pages only name a structure-of-arrays 1-bit layout;
+ *   this library fixes the format): `data` is uint32 [N][K/32] where bit b of
+ *   word w is the sign of column 32w+b, least-significant bit first, 1 = +1 and
+ *   0 = -1; `scales` is IEEE fp16 [N][K/128].  W[n][k] = scales[n][k/128] * sign.
+ *   Requires K % 128 == 0 and dtype TLP_BF16. */
+typedef enum { TLP_W_DENSE = 0, TLP_W_SIGN1_G128 = 1 } tlp_wformat;
+
+typedef struct {
+  int32_t hidden;       /* H; multiple of 8 */
+  int32_t intermediate; /* I; multiple of 8 */
+  int32_t n_q_heads;    /* nq; multiple of n_kv_heads */
+  int32_t n_kv_heads;   /* nkv; nq/nkv in {1, 2, 4} or a multiple of 4 */
+  int32_t head_dim;     /* hd in {64, 128} */
+  int32_t max_seq;      /* cache slots per kv head */
+  int32_t n_layers;     /* layers held by the caches (and by tlp_prefill_chunk) */
+  float rms_eps;        /* eps of every RMSNorm of the layer (incl. QK-norm) */
+  int32_t qk_norm;      /* non-zero: per-head RMSNorm of Q and K before RoPE */
+  int32_t dtype;        /* tlp_dtype */
+  int32_t wformat;      /* tlp_wformat */
+} tlp_config;
+
+/* One projection weight.  Dense: data = [N][K], scales = NULL.
+ * 1-bit: data = sign words, scales = fp16 group scales (see tlp_wformat). */
+typedef struct {
+  const void* data;
+  const void* scales;
+} tlp_weight;
+
+/* Weights of one layer (metal_prefill.rs LayerWeightRefs).  Gains are [H]
+ * (q_norm/k_norm: [hd], shared by all heads; ignored unless qk_norm) in the
+ * config's dtype.  Shapes: w_qkv [(nq+2nkv)hd][H] with Q rows, then K, then V;
+ * w_o [H][nq*hd]; w_gate_up [2I][H] with the gate rows first; w_down [H][I]. */
+typedef struct {
+  const void* attn_norm;
+  tlp_weight w_qkv;
+  const void* q_norm;
+  const void* k_norm;
+  tlp_weight w_o;
+  const void* ffn_norm;
+  tlp_weight w_gate_up;
+  tlp_weight w_down;
+} tlp_layer_weights;
+
+/* Workspace regions (for tlp_workspace_layout).  After tlp_prefill_layer they
+ * hold that call's intermediates: RES fp32 [n][H] residual stream after the
+ * output projection; XN the FFN-normed rows [n][H] (dtype); QKV [n][(nq+2nkv)hd]
+ * with Q normed and roped in place (dtype); ATTN [n][nq*hd] attention output
+ * (dtype); ACT [n][I] SwiGLU output (dtype); HEAD fp32 [H] normed last row
+ * (chunk only). */
+enum { TLP_WS_RES = 0, TLP_WS_XN = 1, TLP_WS_QKV = 2, TLP_WS_ATTN = 3, TLP_WS_ACT = 4,
+       TLP_WS_HEAD = 5, TLP_WS_COUNT = 6 };
+
+/* Bytes of workspace a call with up to `max_tokens` tokens per micro-batch
+ * needs (tlp_prefill_chunk: max_tokens = min(n_tokens, micro_batch)).
+ * Returns 0 for an invalid config or max_tokens <= 0. */
+size_t tlp_workspace_bytes(const tlp_config* cfg, int32_t max_tokens);
+
+/* Byte offsets of the TLP_WS_* regions inside such a workspace (host array
+ * offsets[TLP_WS_COUNT]).  Same validation as tlp_workspace_bytes. */
+tlp_status tlp_workspace_layout(const tlp_config* cfg, int32_t max_tokens, size_t* offsets);
+
+/* RoPE tables on the HOST: cos_host/sin_host [n_pos][head_dim/2] fp32 with
+ * entry [p][i] = cos/sin(p * theta^(-2i/head_dim)), evaluated in double and
+ * rounded once (metal_prefill.rs: host-built cos_table/sin_table of half_dim
+ * entries per position).  The caller uploads them for the rope_cos/rope_sin
+ * arguments below (indexed by absolute position).  head_dim even, > 0. */
+tlp_status tlp_rope_table(double theta, int32_t head_dim, int32_t n_pos, float* cos_host,
+                          float* sin_host);
+
+/* One decoder layer over n_tokens tokens at start_position .. +n_tokens-1
+ * (metal_prefill.rs encode_layer_prefill):
+ *   1 x_n = RMSNorm(x; attn_norm)           2 qkv = W_qkv x_n
+ *   3 optional per-head QK-norm, rotate-half RoPE at the absolute position,
+ *     K (roped) and V (raw) stored to cache[layer][j][start_position + t],
+ *     causal GQA attention of every query over slots [0, its position]
+ *   4 x += W_o attn                         5 x_n2 = RMSNorm(x; ffn_norm)
+ *   6 a = silu(W_gate x_n2) * (W_up x_n2)   7 x += W_down a
+ * hidden: [n_tokens][H] in dtype, read and overwritten in place.  The residual
+ * stream inside the call is fp32.  k_cache, v_cache: [n_layers][nkv][max_seq][hd]
+ * in dtype; exactly the slots [start_position, start_position + n_tokens) of
+ * `layer` are written, slots [0, start_position + n_tokens) of `layer` are read,
+ * and every slot below start_position must already hold that position's K/V.
+ * rope_cos, rope_sin: device fp32 [>= start_position + n_tokens][hd/2].
+ * workspace: device, >= tlp_workspace_bytes(cfg, n_tokens) bytes, 256-aligned. */
+tlp_status tlp_prefill_layer(const tlp_config* cfg, const tlp_layer_weights* weights,
+                             int32_t layer, void* hidden, int32_t n_tokens,
+                             int32_t start_position, void* k_cache, void* v_cache,
+                             const float* rope_cos, const float* rope_sin, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Chunked prefill of n_tokens prompt tokens through all cfg->n_layers layers
+ * (turbospark llama/prefill.rs prefill_chunk_real_llama_dense): micro-batch b
+ * holds tokens [b*micro_batch, min(n_tokens, (b+1)*micro_batch)) at positions
+ * start_position + offset and runs layer 0, 1, ... in order; the residual
+ * stream stays fp32 across layers and is rounded to dtype once per
+ * micro-batch into `hidden` ([n_tokens][H], in place).  layers: host array of
+ * cfg->n_layers weight structs.  If lm_head is not NULL, after the last
+ * micro-batch logits[v] = sum_k lm_head[v][k] * RMSNorm(x_last; final_norm,
+ * final_eps)[k] (fp32 [vocab]); lm_head is [vocab][H] in dtype, final_norm [H]
+ * in dtype.  workspace >= tlp_workspace_bytes(cfg, min(n_tokens, micro_batch)).
+ * The caller tracks the cache position: a chunk must start where the previous
+ * one ended (the stateless library cannot check that). */
+tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* layers,
+                             void* hidden, int32_t n_tokens, int32_t start_position,
+                             int32_t micro_batch, void* k_cache, void* v_cache,
+                             const float* rope_cos, const float* rope_sin,
+                             const void* final_norm, const void* lm_head, int32_t vocab,
+                             float final_eps, float* logits, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Kernels as timed by the profiler below. */
+enum { TLP_K_ATTN_NORM = 0, TLP_K_QKV_GEMM = 1, TLP_K_QK_ROPE_KV = 2, TLP_K_ATTENTION = 3,
+       TLP_K_O_GEMM = 4, TLP_K_FFN_NORM = 5, TLP_K_GATE_UP_GEMM = 6, TLP_K_DOWN_GEMM = 7,
+       TLP_K_FINAL_NORM = 8, TLP_K_LM_HEAD = 9, TLP_K_COUNT = 10 };
+
+/* Per-kernel GPU timing, the analog of the per-layer / per-command-buffer
+ * profiling switches of the pages (metal_full_layer.rs OXIBONSAI_PROFILE and
+ * OXIBONSAI_PROFILE_GPU).  After tlp_profile_begin, every kernel launched by
+ * this thread's tlp_prefill_* calls is bracketed by two HIP events recorded on
+ * the call's stream.  tlp_profile_end waits for those events, writes the
+ * summed elapsed milliseconds and the launch count per TLP_K_* kernel into the
+ * HOST arrays total_ms[TLP_K_COUNT] and launches[TLP_K_COUNT], and stops
+ * recording.  Events are created on first use and reused afterwards. */
+tlp_status tlp_profile_begin(void);
+tlp_status tlp_profile_end(double* total_ms, int32_t* launches);
+
+/* Static text of a status code. */
+const char* tlp_status_string(tlp_status status);
+
+/* Text of the calling thread's most recent error ("" if none). */
+const char* tlp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TLP_H */

@@ -1,0 +1,112 @@
+"""Shared plumbing of the GPU parity tests: run the HIP library through the C
+ABI on seeded synthetic inputs and run the float64 oracle on the same inputs.
+
+Error metric: for a checked tensor, max|gpu - oracle| / max|oracle| (the
+infinity-norm relative error), computed in float64.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+
+BF16_TOL = 2e-2   # bf16 inputs, fp32 accumulation
+F32_TOL = 1e-4    # fp32 path
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "non-finite values in the GPU result"
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def tol_of(shape) -> float:
+    return F32_TOL if shape.dtype == "f32" else BF16_TOL
+
+
+class GpuRun:
+    """Device-resident inputs of one shape, plus the calls into the library."""
+
+    def __init__(self, shape, layers_np: list, x_np, kc_np, vc_np, device="cuda"):
+        import torch
+        from transformer_layer_prefill_amd import tensors
+        import transformer_layer_prefill_amd as tlp
+        self.torch, self.tensors, self.tlp = torch, tensors, tlp
+        self.shape = shape
+        self.cfg = tensors.config_of(shape)
+        self.layers = [tensors.DeviceLayer(w, device) for w in layers_np]
+        self.hidden = tensors.to_device(x_np, device)
+        self.kc = tensors.to_device(kc_np, device)
+        self.vc = tensors.to_device(vc_np, device)
+        cos, sin = tlp.rope_table(shape.theta, shape.head_dim, shape.max_seq)
+        self.cos = tensors.to_device(cos, device)
+        self.sin = tensors.to_device(sin, device)
+        self.ws = None
+
+    def workspace(self, max_tokens):
+        nbytes = self.tlp.workspace_bytes(self.cfg, max_tokens)
+        if self.ws is None or self.ws.numel() < nbytes:
+            self.ws = self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.hidden.device)
+        return self.ws
+
+    def layer(self, layer: int, n: int, start: int, hidden=None):
+        h = self.hidden if hidden is None else hidden
+        ws = self.workspace(n)
+        self.tlp.prefill_layer(self.cfg, self.layers[layer].struct, layer, h, n, start, self.kc,
+                               self.vc, self.cos, self.sin, ws)
+        self.torch.cuda.synchronize()
+
+    def chunk(self, n: int, start: int, mb: int, hidden=None, head=None):
+        h = self.hidden if hidden is None else hidden
+        ws = self.workspace(min(n, mb))
+        kw = {}
+        if head is not None:
+            fn, W, vocab, logits = head
+            kw = dict(final_norm=fn, lm_head=W, vocab=vocab, final_eps=self.shape.eps,
+                      logits=logits)
+        self.tlp.prefill_chunk(self.cfg, [d.struct for d in self.layers], h, n, start, mb,
+                               self.kc, self.vc, self.cos, self.sin, ws, **kw)
+        self.torch.cuda.synchronize()
+
+    def host(self, t):
+        return self.tensors.to_host(t)
+
+
+def widen_caches(shape, kc, vc):
+    return synth.widen(kc, shape.dtype), synth.widen(vc, shape.dtype)
+
+
+def oracle_layer(shape, w_np, layer, x_np, kc_np, vc_np, rows=None):
+    """Oracle of one layer on storage-format inputs; returns (out, kc64, vc64)."""
+    w64 = synth.widen_layer(shape, w_np)
+    x64 = synth.widen(x_np, shape.dtype)
+    kc64, vc64 = widen_caches(shape, kc_np, vc_np)
+    out = oracle.prefill_layer(shape, w64, layer, x64, shape.start, kc64, vc64, rows=rows)
+    return out, kc64, vc64
+
+
+def check_cache_slots(shape, layer, n, start, kc_in, kc_gpu):
+    """Bit-exact slot indexing: exactly the slots [start, start+n) of `layer` differ.
+
+    The input caches hold a NaN sentinel in every slot at or after `start`,
+    so every written slot must change (to finite values) and every other slot
+    must keep its bits.
+    """
+    u = np.uint16 if kc_in.dtype == np.uint16 else np.uint32
+    slot_changed = (kc_gpu.view(u) != kc_in.view(u)).any(axis=-1)      # [L][nkv][max_seq]
+    expect = np.zeros_like(slot_changed)
+    expect[layer, :, start:start + n] = True
+    written = synth.widen(kc_gpu[layer, :, start:start + n], shape.dtype)
+    assert np.all(np.isfinite(written)), "a written cache slot holds non-finite values"
+    assert np.array_equal(slot_changed, expect), "cache slots changed outside [start, start+n)"

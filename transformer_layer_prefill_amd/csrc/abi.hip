@@ -1,0 +1,432 @@
+// C-ABI entry points: argument validation, workspace layout and the launch
+// sequence of one layer / one chunk.  See include/tlp.h for the contract.
+//
+// Launch sequence of a layer (oxibonsai-kernels metal_prefill.rs,
+// encode_layer_prefill steps 1-7), all on the caller's stream, no host sync:
+//   rmsnorm (+ fp32 copy of the residual) -> QKV GEMM -> QK-norm/RoPE/KV store
+//   -> attention -> O GEMM (+ residual, fp32) -> rmsnorm -> gate/up GEMM with
+//   SwiGLU -> down GEMM (+ residual)
+// The chunk driver (turbospark-runtime llama/prefill.rs,
+// prefill_chunk_real_llama_dense) runs that per micro-batch and per layer,
+// keeping the residual stream in fp32 between layers.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/tlp.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tlp_status fail(tlp_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tlp_status fail(tlp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t elt_size(const tlp_config& c) { return c.dtype == TLP_F32 ? 4 : 2; }
+
+tlp_status check_config(const tlp_config* c) {
+  if (!c) return fail(TLP_ERR_NULL, "config is NULL");
+  if (c->dtype != TLP_F32 && c->dtype != TLP_BF16)
+    return fail(TLP_ERR_UNSUPPORTED, "dtype %d is not TLP_F32 or TLP_BF16", c->dtype);
+  if (c->wformat != TLP_W_DENSE && c->wformat != TLP_W_SIGN1_G128)
+    return fail(TLP_ERR_UNSUPPORTED, "wformat %d is not a tlp_wformat", c->wformat);
+  if (c->wformat == TLP_W_SIGN1_G128 && c->dtype != TLP_BF16)
+    return fail(TLP_ERR_UNSUPPORTED, "1-bit weights need dtype TLP_BF16");
+  if (c->hidden <= 0 || c->intermediate <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->max_seq <= 0 || c->n_layers <= 0)
+    return fail(TLP_ERR_SHAPE, "sizes must be positive");
+  if (c->hidden % 8 || c->intermediate % 8)
+    return fail(TLP_ERR_SHAPE, "hidden (%d) and intermediate (%d) must be multiples of 8",
+                c->hidden, c->intermediate);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(TLP_ERR_SHAPE, "head_dim %d is not 64 or 128", c->head_dim);
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(TLP_ERR_SHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                c->n_q_heads, c->n_kv_heads);
+  const int g = c->n_q_heads / c->n_kv_heads;
+  if (!(g == 1 || g == 2 || g == 4 || g % 4 == 0))
+    return fail(TLP_ERR_UNSUPPORTED, "heads per kv group %d is not 1, 2 or a multiple of 4", g);
+  if (c->wformat == TLP_W_SIGN1_G128 &&
+      (c->hidden % 128 || c->intermediate % 128 || (c->n_q_heads * c->head_dim) % 128))
+    return fail(TLP_ERR_SHAPE, "1-bit weights need every K (hidden, intermediate, nq*hd) "
+                               "to be a multiple of 128");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps))
+    return fail(TLP_ERR_SHAPE, "rms_eps must be finite and >= 0");
+  return TLP_OK;
+}
+
+struct Layout {
+  size_t off[TLP_WS_COUNT];
+  size_t total;
+};
+
+Layout layout_of(const tlp_config& c, int m) {
+  const size_t e = elt_size(c), M = static_cast<size_t>(m);
+  const size_t qkv = static_cast<size_t>(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const size_t sizes[TLP_WS_COUNT] = {
+      M * c.hidden * 4,                                       // RES
+      M * c.hidden * e,                                       // XN
+      M * qkv * e,                                            // QKV
+      M * static_cast<size_t>(c.n_q_heads) * c.head_dim * e,  // ATTN
+      M * c.intermediate * e,                                 // ACT
+      static_cast<size_t>(c.hidden) * 4,                      // HEAD
+  };
+  Layout L{};
+  size_t o = 0;
+  for (int i = 0; i < TLP_WS_COUNT; ++i) {
+    L.off[i] = o;
+    o += align256(sizes[i]);
+  }
+  L.total = o;
+  return L;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+tlp_status check_weight(const tlp_config& c, const tlp_weight& w, const char* name) {
+  if (!w.data) return fail(TLP_ERR_NULL, "weight %s is NULL", name);
+  if (c.wformat == TLP_W_SIGN1_G128 && !w.scales)
+    return fail(TLP_ERR_NULL, "1-bit weight %s has no scales", name);
+  if (!aligned16(w.data))
+    return fail(TLP_ERR_UNSUPPORTED, "weight %s is not 16-byte aligned", name);
+  return TLP_OK;
+}
+
+tlp_status check_layer_weights(const tlp_config& c, const tlp_layer_weights* w, int idx) {
+  if (!w) return fail(TLP_ERR_NULL, "layer weights are NULL");
+  if (!w->attn_norm || !w->ffn_norm)
+    return fail(TLP_ERR_NULL, "layer %d: a norm gain is NULL", idx);
+  if (c.qk_norm && (!w->q_norm || !w->k_norm))
+    return fail(TLP_ERR_NULL, "layer %d: qk_norm is on but q_norm/k_norm is NULL", idx);
+  if (!aligned16(w->attn_norm) || !aligned16(w->ffn_norm))
+    return fail(TLP_ERR_UNSUPPORTED, "layer %d: norm gains must be 16-byte aligned", idx);
+  tlp_status s;
+  if ((s = check_weight(c, w->w_qkv, "w_qkv")) != TLP_OK) return s;
+  if ((s = check_weight(c, w->w_o, "w_o")) != TLP_OK) return s;
+  if ((s = check_weight(c, w->w_gate_up, "w_gate_up")) != TLP_OK) return s;
+  if ((s = check_weight(c, w->w_down, "w_down")) != TLP_OK) return s;
+  return TLP_OK;
+}
+
+tlp_status check_call(const tlp_config& c, void* hidden, int n, int start, void* kc, void* vc,
+                      const float* cs, const float* sn, void* ws, size_t ws_bytes, int m_ws) {
+  if (!hidden || !kc || !vc || !cs || !sn || !ws)
+    return fail(TLP_ERR_NULL, "hidden, caches, rope tables and workspace must be non-NULL");
+  if (n <= 0) return fail(TLP_ERR_SHAPE, "n_tokens %d must be > 0", n);
+  if (start < 0) return fail(TLP_ERR_POSITION, "start_position %d is negative", start);
+  if (static_cast<int64_t>(start) + n > c.max_seq)
+    return fail(TLP_ERR_POSITION, "start_position %d + n_tokens %d exceeds max_seq %d", start,
+                n, c.max_seq);
+  if (!aligned16(hidden) || !aligned16(kc) || !aligned16(vc))
+    return fail(TLP_ERR_UNSUPPORTED, "hidden and caches must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return fail(TLP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = layout_of(c, m_ws).total;
+  if (ws_bytes < need)
+    return fail(TLP_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return TLP_OK;
+}
+
+// ---- per-kernel timing with HIP events (tlp_profile_begin / tlp_profile_end) --
+// While a thread has profiling on, every launch it makes is bracketed by two
+// events recorded on the launch's own stream; tlp_profile_end waits for them
+// and sums the elapsed times per kernel.
+struct ProfRecord {
+  int kernel;
+  hipEvent_t start, stop;
+};
+thread_local bool g_prof_on = false;
+thread_local std::vector<ProfRecord> g_prof;
+thread_local std::vector<hipEvent_t> g_event_pool;
+
+hipError_t take_event(hipEvent_t* e) {
+  if (!g_event_pool.empty()) {
+    *e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(e);
+}
+
+struct ProfScope {
+  int kernel;
+  hipStream_t s;
+  hipEvent_t start = nullptr;
+  hipError_t err = hipSuccess;
+  ProfScope(int k, hipStream_t st) : kernel(k), s(st) {
+    if (!g_prof_on) return;
+    if ((err = take_event(&start)) == hipSuccess) err = hipEventRecord(start, s);
+  }
+  hipError_t finish() {
+    if (!g_prof_on || err != hipSuccess) return err;
+    hipEvent_t stop;
+    if ((err = take_event(&stop)) != hipSuccess) return err;
+    if ((err = hipEventRecord(stop, s)) != hipSuccess) return err;
+    g_prof.push_back({kernel, start, stop});
+    return hipSuccess;
+  }
+};
+
+#define TLP_LAUNCH(kid, expr)                                                     \
+  do {                                                                            \
+    ProfScope ps_(kid, s);                                                        \
+    hipError_t e_ = ps_.err == hipSuccess ? (expr) : ps_.err;                     \
+    if (e_ == hipSuccess) e_ = ps_.finish();                                      \
+    if (e_ != hipSuccess)                                                         \
+      return fail(TLP_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_));           \
+  } while (0)
+
+// One layer over the rows already in the workspace / hidden.  x_in: the rows'
+// input (hidden in act type when x_in_f32 is false, else the fp32 residual
+// stream); out_act: when non-null the down projection writes dtype rows there,
+// otherwise it updates the fp32 residual stream in place.
+tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer, int n,
+                     int start, const void* x_in, bool x_in_f32, void* out_act, char* kc,
+                     char* vc, const float* cs, const float* sn, char* ws, const Layout& L,
+                     hipStream_t s) {
+  using namespace tlp;
+  const Act act = c.dtype == TLP_F32 ? Act::F32 : Act::BF16;
+  const int H = c.hidden, I = c.intermediate, hd = c.head_dim;
+  const int nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const int qkv_dim = (nq + 2 * nkv) * hd, qd = nq * hd;
+  float* res = reinterpret_cast<float*>(ws + L.off[TLP_WS_RES]);
+  void* xn = ws + L.off[TLP_WS_XN];
+  void* qkv = ws + L.off[TLP_WS_QKV];
+  void* attn = ws + L.off[TLP_WS_ATTN];
+  void* a = ws + L.off[TLP_WS_ACT];
+  const size_t es = elt_size(c);
+  const size_t layer_off = static_cast<size_t>(layer) * nkv * c.max_seq * hd * es;
+  void* k_layer = kc + layer_off;
+  void* v_layer = vc + layer_off;
+
+  // 1. attention RMSNorm (fp32 copy of the input rows becomes the residual stream)
+  TLP_LAUNCH(TLP_K_ATTN_NORM, launch_rmsnorm(act, x_in, x_in_f32, H, x_in_f32 ? nullptr : res, w.attn_norm, xn,
+                            false, n, H, c.rms_eps, s));
+  // 2. fused QKV projection
+  GemmCall g{};
+  g.act = act;
+  g.A = xn; g.lda = H;
+  g.W = w.w_qkv.data; g.Wscale = w.w_qkv.scales;
+  g.M = n; g.N = qkv_dim; g.K = H;
+  g.epi = Epi::Store; g.out = qkv; g.ldo = qkv_dim;
+  TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemm(g, s));
+  // 3a-3d. QK-norm, RoPE, KV-cache store
+  TLP_LAUNCH(TLP_K_QK_ROPE_KV, launch_qk_rope_store(act, qkv, n, qkv_dim, w.q_norm, w.k_norm, c.qk_norm != 0,
+                                  c.rms_eps, cs, sn, k_layer, v_layer, c.max_seq, start, nq, nkv,
+                                  hd, s));
+  // 3e. causal GQA attention
+  TLP_LAUNCH(TLP_K_ATTENTION, launch_attention(act, qkv, qkv_dim, k_layer, v_layer, attn, qd, n, start, nq, nkv,
+                              hd, c.max_seq, s));
+  // 4. output projection + residual (fp32 stream, in place)
+  g = GemmCall{};
+  g.act = act;
+  g.A = attn; g.lda = qd;
+  g.W = w.w_o.data; g.Wscale = w.w_o.scales;
+  g.M = n; g.N = H; g.K = qd;
+  g.epi = Epi::Resid; g.out = res; g.ldo = H; g.out_f32 = true; g.resid = res; g.ldr = H;
+  TLP_LAUNCH(TLP_K_O_GEMM, launch_gemm(g, s));
+  // 5. FFN RMSNorm
+  TLP_LAUNCH(TLP_K_FFN_NORM, launch_rmsnorm(act, res, true, H, nullptr, w.ffn_norm, xn, false, n, H, c.rms_eps,
+                            s));
+  // 6. gate/up projection + SwiGLU
+  g = GemmCall{};
+  g.act = act;
+  g.A = xn; g.lda = H;
+  g.W = w.w_gate_up.data; g.Wscale = w.w_gate_up.scales;
+  g.M = n; g.N = I; g.K = H;
+  g.epi = Epi::SwiGLU; g.out = a; g.ldo = I;
+  TLP_LAUNCH(TLP_K_GATE_UP_GEMM, launch_gemm(g, s));
+  // 7. down projection + residual
+  g = GemmCall{};
+  g.act = act;
+  g.A = a; g.lda = I;
+  g.W = w.w_down.data; g.Wscale = w.w_down.scales;
+  g.M = n; g.N = H; g.K = I;
+  g.epi = Epi::Resid; g.resid = res; g.ldr = H; g.ldo = H;
+  if (out_act) {
+    g.out = out_act;
+    g.out_f32 = act == Act::F32;
+  } else {
+    g.out = res;
+    g.out_f32 = true;
+  }
+  TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm(g, s));
+  return TLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tlp_workspace_bytes(const tlp_config* cfg, int32_t max_tokens) {
+  if (check_config(cfg) != TLP_OK || max_tokens <= 0) return 0;
+  return layout_of(*cfg, max_tokens).total;
+}
+
+tlp_status tlp_workspace_layout(const tlp_config* cfg, int32_t max_tokens, size_t* offsets) {
+  tlp_status s = check_config(cfg);
+  if (s != TLP_OK) return s;
+  if (!offsets) return fail(TLP_ERR_NULL, "offsets is NULL");
+  if (max_tokens <= 0) return fail(TLP_ERR_SHAPE, "max_tokens must be > 0");
+  const Layout L = layout_of(*cfg, max_tokens);
+  for (int i = 0; i < TLP_WS_COUNT; ++i) offsets[i] = L.off[i];
+  return TLP_OK;
+}
+
+tlp_status tlp_rope_table(double theta, int32_t head_dim, int32_t n_pos, float* cos_host,
+                          float* sin_host) {
+  if (!cos_host || !sin_host) return fail(TLP_ERR_NULL, "table pointers are NULL");
+  if (head_dim <= 0 || head_dim % 2 || n_pos <= 0)
+    return fail(TLP_ERR_SHAPE, "head_dim must be even and positive, n_pos positive");
+  if (!(theta > 0.0) || !std::isfinite(theta)) return fail(TLP_ERR_SHAPE, "theta must be > 0");
+  const int half = head_dim / 2;
+  for (int i = 0; i < half; ++i) {
+    const double f = std::pow(theta, -2.0 * i / head_dim);
+    for (int p = 0; p < n_pos; ++p) {
+      const double ang = static_cast<double>(p) * f;
+      cos_host[static_cast<size_t>(p) * half + i] = static_cast<float>(std::cos(ang));
+      sin_host[static_cast<size_t>(p) * half + i] = static_cast<float>(std::sin(ang));
+    }
+  }
+  return TLP_OK;
+}
+
+tlp_status tlp_prefill_layer(const tlp_config* cfg, const tlp_layer_weights* weights,
+                             int32_t layer, void* hidden, int32_t n_tokens,
+                             int32_t start_position, void* k_cache, void* v_cache,
+                             const float* rope_cos, const float* rope_sin, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  tlp_status s = check_config(cfg);
+  if (s != TLP_OK) return s;
+  if (layer < 0 || layer >= cfg->n_layers)
+    return fail(TLP_ERR_SHAPE, "layer %d outside [0, %d)", layer, cfg->n_layers);
+  if ((s = check_layer_weights(*cfg, weights, layer)) != TLP_OK) return s;
+  if ((s = check_call(*cfg, hidden, n_tokens, start_position, k_cache, v_cache, rope_cos,
+                      rope_sin, workspace, workspace_bytes, n_tokens > 0 ? n_tokens : 1)) != TLP_OK)
+    return s;
+  const Layout L = layout_of(*cfg, n_tokens);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  g_last_error.clear();
+  return run_layer(*cfg, *weights, layer, n_tokens, start_position, hidden, false, hidden,
+                   static_cast<char*>(k_cache), static_cast<char*>(v_cache), rope_cos, rope_sin,
+                   static_cast<char*>(workspace), L, st);
+}
+
+tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* layers,
+                             void* hidden, int32_t n_tokens, int32_t start_position,
+                             int32_t micro_batch, void* k_cache, void* v_cache,
+                             const float* rope_cos, const float* rope_sin,
+                             const void* final_norm, const void* lm_head, int32_t vocab,
+                             float final_eps, float* logits, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  tlp_status s = check_config(cfg);
+  if (s != TLP_OK) return s;
+  if (!layers) return fail(TLP_ERR_NULL, "layers is NULL");
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if ((s = check_layer_weights(*cfg, &layers[l], l)) != TLP_OK) return s;
+  if (micro_batch <= 0) return fail(TLP_ERR_SHAPE, "micro_batch %d must be > 0", micro_batch);
+  const int mb = n_tokens < micro_batch ? n_tokens : micro_batch;
+  if ((s = check_call(*cfg, hidden, n_tokens, start_position, k_cache, v_cache, rope_cos,
+                      rope_sin, workspace, workspace_bytes, mb > 0 ? mb : 1)) != TLP_OK)
+    return s;
+  if (lm_head) {
+    if (!final_norm || !logits) return fail(TLP_ERR_NULL, "lm_head needs final_norm and logits");
+    if (vocab <= 0) return fail(TLP_ERR_SHAPE, "vocab %d must be > 0", vocab);
+    if (!aligned16(lm_head) || !aligned16(final_norm))
+      return fail(TLP_ERR_UNSUPPORTED, "lm_head and final_norm must be 16-byte aligned");
+    if (!(final_eps >= 0.f) || !std::isfinite(final_eps))
+      return fail(TLP_ERR_SHAPE, "final_eps must be finite and >= 0");
+  }
+  using namespace tlp;
+  const Act act = cfg->dtype == TLP_F32 ? Act::F32 : Act::BF16;
+  const Layout L = layout_of(*cfg, mb);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const size_t row_bytes = static_cast<size_t>(cfg->hidden) * elt_size(*cfg);
+  g_last_error.clear();
+  for (int off = 0; off < n_tokens; off += mb) {
+    const int m = n_tokens - off < mb ? n_tokens - off : mb;
+    char* rows = static_cast<char*>(hidden) + static_cast<size_t>(off) * row_bytes;
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      const bool first = l == 0, last = l == cfg->n_layers - 1;
+      s = run_layer(*cfg, layers[l], l, m, start_position + off,
+                    first ? static_cast<const void*>(rows) : ws + L.off[TLP_WS_RES], !first,
+                    last ? rows : nullptr, static_cast<char*>(k_cache),
+                    static_cast<char*>(v_cache), rope_cos, rope_sin, ws, L, st);
+      if (s != TLP_OK) return s;
+    }
+  }
+  if (lm_head) {
+    hipStream_t s = st;
+    const char* last_row = static_cast<char*>(hidden) + static_cast<size_t>(n_tokens - 1) * row_bytes;
+    float* xh = reinterpret_cast<float*>(ws + L.off[TLP_WS_HEAD]);
+    TLP_LAUNCH(TLP_K_FINAL_NORM, launch_rmsnorm(act, last_row, false, cfg->hidden, nullptr, final_norm, xh, true, 1,
+                              cfg->hidden, final_eps, st));
+    TLP_LAUNCH(TLP_K_LM_HEAD, launch_lm_head(act, xh, lm_head, logits, vocab, cfg->hidden, s));
+  }
+  return TLP_OK;
+}
+
+tlp_status tlp_profile_begin(void) {
+  for (auto& r : g_prof) {
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_prof.clear();
+  g_prof_on = true;
+  return TLP_OK;
+}
+
+tlp_status tlp_profile_end(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return fail(TLP_ERR_NULL, "output arrays are NULL");
+  g_prof_on = false;
+  for (int k = 0; k < TLP_K_COUNT; ++k) {
+    total_ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  tlp_status st = TLP_OK;
+  for (auto& r : g_prof) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess && st == TLP_OK)
+      st = fail(TLP_ERR_HIP, "profile events: %s", hipGetErrorString(e));
+    total_ms[r.kernel] += ms;
+    launches[r.kernel] += 1;
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_prof.clear();
+  return st;
+}
+
+const char* tlp_status_string(tlp_status status) {
+  switch (status) {
+    case TLP_OK: return "ok";
+    case TLP_ERR_NULL: return "null pointer";
+    case TLP_ERR_SHAPE: return "invalid shape";
+    case TLP_ERR_POSITION: return "position out of range";
+    case TLP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TLP_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case TLP_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* tlp_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,279 @@
+// Causal grouped-query attention over the KV cache for every query row of a
+// micro-batch at once (oxibonsai-kernels metal_prefill.rs, encode_layer_prefill
+// step 3e: scores q.K/sqrt(hd) over seq_len = pos + 1 keys, softmax, weighted
+// sum of V; query head h reads kv head h / heads_per_group).  The pages run it
+// one query position at a time with a materialised score row; here it is one
+// flash-style kernel with an online softmax and no score buffer.
+//
+// bf16 kernel (gfx950 MFMA).  A block owns one kv head and a tile of query
+// tokens; its four wavefronts are (query head of the group, 32-token slice)
+// pairs that share every K/V block staged in LDS, so K/V are read once per
+// group.  Per 64-key block a wavefront computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 (lane = query, 32 key scores per lane), runs the
+// online softmax in fp32 with exp2, and accumulates O^T = V^T P^T, taking P
+// straight from the score registers and V^T from a transposed LDS copy.
+#include "common.h"
+#include "launch.h"
+
+namespace tlp {
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  int q_ld, out_ld;
+  int M, start, nq, nkv, max_seq;
+  int group;      // nq / nkv
+  int hpb;        // query heads per block (min(group, 4))
+  int tiles;      // token tiles
+  float scale_log2;  // log2(e) / sqrt(hd)
+};
+
+template <int HD>
+__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a) {
+  constexpr int KB = 64;        // keys per block
+  constexpr int KLD = HD + 8;   // K row stride in LDS (elements)
+  constexpr int VLD = KB + 8;   // V^T row stride in LDS (elements)
+  constexpr int KS = HD / 16;   // k-steps of the QK^T contraction
+  constexpr int DB = HD / 32;   // 32-wide blocks of the head dimension
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * VLD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int hpb = a.hpb;
+  const int tsub = 4 / hpb;            // 32-token slices per block
+  const int bt = 32 * tsub;            // tokens per block
+  const int tile = a.tiles - 1 - static_cast<int>(blockIdx.x);  // longest rows first
+  const int quads = a.group / hpb;
+  const int j = blockIdx.y / quads, quad = blockIdx.y % quads;
+  const int h = j * a.group + quad * hpb + wave % hpb;
+  const int t = tile * bt + (wave / hpb) * 32 + lr;   // this lane's query token
+  const bool q_ok = t < a.M;
+  const int pos = a.start + (q_ok ? t : 0);
+
+  // Q^T fragments (B operand): lane holds Q[t][ks*16 + lh*8 .. +8]
+  bf16x8_t qf[KS];
+  {
+    const uint16_t* qrow = a.q + static_cast<size_t>(q_ok ? t : 0) * a.q_ld + h * HD;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 u = q_ok ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + lh * 8)
+                     : make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  }
+
+  const int last_tok = min(a.M, (tile + 1) * bt) - 1;
+  const int kv_end = a.start + last_tok + 1;          // keys this block may need
+  const int nkb = (kv_end + KB - 1) / KB;
+  const uint16_t* kbase = a.k + static_cast<size_t>(j) * a.max_seq * HD;
+  const uint16_t* vbase = a.v + static_cast<size_t>(j) * a.max_seq * HD;
+
+  f32x16_t o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int key0 = kb * KB;
+    __syncthreads();
+    // stage K rows [key0, key0 + 64) and V^T; rows past kv_end are zero so an
+    // unwritten (possibly NaN) cache slot never reaches the products
+    for (int c = tid; c < KB * HD / 8; c += 256) {
+      const int row = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+      const int key = key0 + row;
+      uint4 u = key < kv_end
+                    ? *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(key) * HD + cc)
+                    : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&Ks[row * KLD + cc]) = u;
+    }
+    for (int c = tid; c < (KB / 2) * (HD / 8); c += 256) {
+      const int kp = c % (KB / 2), dc = (c / (KB / 2)) * 8;
+      const int key = key0 + 2 * kp;
+      uint4 u0 = key < kv_end
+                     ? *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(key) * HD + dc)
+                     : make_uint4(0, 0, 0, 0);
+      uint4 u1 = key + 1 < kv_end ? *reinterpret_cast<const uint4*>(
+                                        vbase + static_cast<size_t>(key + 1) * HD + dc)
+                                  : make_uint4(0, 0, 0, 0);
+      const uint32_t w0[4] = {u0.x, u0.y, u0.z, u0.w};
+      const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<uint32_t*>(&Vt[(dc + 2 * e) * VLD + 2 * kp]) =
+            (w0[e] & 0xffffu) | (w1[e] << 16);
+        *reinterpret_cast<uint32_t*>(&Vt[(dc + 2 * e + 1) * VLD + 2 * kp]) =
+            (w0[e] >> 16) | (w1[e] & 0xffff0000u);
+      }
+    }
+    __syncthreads();
+
+    // S^T for two 32-key halves: lane (query lr) gets keys 8*(r/4) + 4*lh + r%4
+    f32x16_t s[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[hb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[(hb * 32 + lr) * KLD + ks * 16 + lh * 8]);
+        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[hb], 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + hb * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+        const float v = key <= pos ? s[hb][r] * a.scale_log2 : -INFINITY;
+        s[hb][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);     // finite: key 0 is visible to every row
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.f;
+    bf16x8_t pf[4];   // B operand of step 2*hb + half: slots (lh, e) <- r = 8*half + e
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(s[hb][r] - m_new);
+        psum += p;
+        pf[hb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p);
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+
+    // O^T += V^T P^T.  Slot (lh, e) of step (hb, half) is key
+    // hb*32 + half*16 + 8*(e/4) + 4*lh + e%4, matching the score layout above.
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      const uint16_t* vrow = &Vt[(d * 32 + lr) * VLD];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int base = (st >> 1) * 32 + (st & 1) * 16 + lh * 4;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + base);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + base + 8);
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], o[d], 0, 0, 0);
+      }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!q_ok) return;
+  const float inv = 1.0f / l_tot;
+  uint16_t* orow = a.out + static_cast<size_t>(t) * a.out_ld + h * HD;
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dd = d * 32 + r4 * 8 + lh * 4;
+      uint2 w;
+      w.x = pack_bf16x2(o[d][r4 * 4 + 0] * inv, o[d][r4 * 4 + 1] * inv);
+      w.y = pack_bf16x2(o[d][r4 * 4 + 2] * inv, o[d][r4 * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + dd) = w;
+    }
+}
+
+// fp32 kernel: one block per (query token, query head); keys in chunks of
+// 256 with an online softmax in fp32 using expf.
+__global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__ q, int q_ld,
+                                                       const float* __restrict__ k_layer,
+                                                       const float* __restrict__ v_layer,
+                                                       float* __restrict__ out, int out_ld,
+                                                       int start, int nq, int nkv, int hd,
+                                                       int max_seq, float scale) {
+  __shared__ float qs[128];
+  __shared__ float p[256];
+  __shared__ float red[4];
+  const int t = blockIdx.x, h = blockIdx.y;
+  const int j = h / (nq / nkv);
+  const int n_keys = start + t + 1;
+  const int tid = threadIdx.x;
+  if (tid < hd) qs[tid] = q[static_cast<size_t>(t) * q_ld + h * hd + tid];
+  __syncthreads();
+  const float* kb = k_layer + static_cast<size_t>(j) * max_seq * hd;
+  const float* vb = v_layer + static_cast<size_t>(j) * max_seq * hd;
+  float m_run = -INFINITY, l_run = 0.f, acc = 0.f;
+  for (int base = 0; base < n_keys; base += 256) {
+    const int u = base + tid;
+    float s = -INFINITY;
+    if (u < n_keys) {
+      const float* kr = kb + static_cast<size_t>(u) * hd;
+      float d = 0.f;
+      for (int e = 0; e < hd; ++e) d = fmaf(qs[e], kr[e], d);
+      s = d * scale;
+    }
+    // block max
+    float mx = wave_max(s);
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    const float m_new = fmaxf(m_run, mx);
+    const float pe = u < n_keys ? expf(s - m_new) : 0.f;
+    p[tid] = pe;
+    const float bs = block_sum<4>(pe, red);   // its barriers also publish p[]
+    const float alpha = expf(m_run - m_new);
+    l_run = l_run * alpha + bs;
+    if (tid < hd) {
+      float a2 = acc * alpha;
+      const int cnt = min(256, n_keys - base);
+      for (int uu = 0; uu < cnt; ++uu) a2 = fmaf(p[uu], vb[static_cast<size_t>(base + uu) * hd + tid], a2);
+      acc = a2;
+    }
+    m_run = m_new;
+    __syncthreads();
+  }
+  if (tid < hd) out[static_cast<size_t>(t) * out_ld + h * hd + tid] = acc / l_run;
+}
+
+hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_layer,
+                            const void* v_layer, void* out, int out_ld, int M, int start,
+                            int nq, int nkv, int head_dim, int max_seq, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (act == Act::F32) {
+    dim3 grid(M, nq);
+    attn_f32_kernel<<<grid, 256, 0, s>>>(
+        static_cast<const float*>(q), q_ld, static_cast<const float*>(k_layer),
+        static_cast<const float*>(v_layer), static_cast<float*>(out), out_ld, start, nq, nkv,
+        head_dim, max_seq, 1.0f / sqrtf(static_cast<float>(head_dim)));
+    return hipGetLastError();
+  }
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_layer);
+  a.v = static_cast<const uint16_t*>(v_layer);
+  a.out = static_cast<uint16_t*>(out);
+  a.q_ld = q_ld;
+  a.out_ld = out_ld;
+  a.M = M;
+  a.start = start;
+  a.nq = nq;
+  a.nkv = nkv;
+  a.max_seq = max_seq;
+  a.group = nq / nkv;
+  a.hpb = a.group < 4 ? a.group : 4;
+  const int bt = 32 * (4 / a.hpb);
+  a.tiles = (M + bt - 1) / bt;
+  a.scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
+  dim3 grid(a.tiles, nkv * (a.group / a.hpb));
+  if (head_dim == 128)
+    attn_fwd_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
+  else
+    attn_fwd_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace tlp

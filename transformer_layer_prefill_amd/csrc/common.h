@@ -1,0 +1,73 @@
+// Shared device helpers for the gfx950 prefill kernels: element types,
+// conversions, vector types for the MFMA builtins and wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tlp {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// bf16 values travel as raw 16-bit patterns in memory.
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (gfx950 has a hardware convert).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Element access for the two activation types (fp32 or bf16 bit patterns).
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static __device__ __forceinline__ float ld(float v) { return v; }
+  static __device__ __forceinline__ float st(float v) { return v; }
+};
+template <> struct Elt<uint16_t> {
+  static __device__ __forceinline__ float ld(uint16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ uint16_t st(float v) { return f32_to_bf16(v); }
+};
+
+template <typename T> __device__ __forceinline__ float to_f32(T v) { return Elt<T>::ld(v); }
+template <typename T> __device__ __forceinline__ T from_f32(float v) { return Elt<T>::st(v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Block-wide sum for blockDim.x == 64 * NW; every thread receives the total.
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* red /* LDS, NW floats */) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+}  // namespace tlp

@@ -1,0 +1,238 @@
+// Row-wise, HBM-bound kernels of the layer: RMSNorm of token rows, the fused
+// QK-norm + RoPE + KV-cache store, the fp32 -> activation row store and the
+// last-token LM-head GEMV.
+//
+// Operations follow oxibonsai-kernels metal_prefill.rs, encode_layer_prefill
+// steps 1 and 5 (batched RMSNorm), step 3a-3d (QK-norm, RoPE, KV store) and
+// the "Tail" block of encode_full_forward_prefill (final norm + LM head).
+#include "common.h"
+#include "launch.h"
+
+namespace tlp {
+
+// 8 consecutive elements <-> 8 floats; p must be 16-byte aligned for bf16 and
+// 32-byte aligned for fp32 (rows are multiples of 8 elements).
+__device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float v[8]) {
+  uint4 u;
+  u.x = pack_bf16x2(v[0], v[1]);
+  u.y = pack_bf16x2(v[2], v[3]);
+  u.z = pack_bf16x2(v[4], v[5]);
+  u.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// One 256-thread block per row.  Pass 1 sums squares (fp32), pass 2 re-reads
+// the row (an L1/L2 hit) and writes gain * x * rsqrt(mean + eps).
+template <typename TX, typename TG, typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, int ldx,
+                                                      float* __restrict__ res_copy,
+                                                      const TG* __restrict__ gain,
+                                                      TO* __restrict__ out, int H, float eps) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const TX* xr = x + static_cast<size_t>(r) * ldx;
+  const int chunks = H >> 3;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    float v[8];
+    load8(xr + c * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+    if (res_copy) store8(res_copy + static_cast<size_t>(r) * H + c * 8, v);
+  }
+  ss = block_sum<4>(ss, red);
+  const float inv = rsqrtf(ss / static_cast<float>(H) + eps);
+  TO* orow = out + static_cast<size_t>(r) * H;
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    float v[8], g[8];
+    load8(xr + c * 8, v);
+    load8(gain + c * 8, g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = g[i] * (v[i] * inv);
+    store8(orow + c * 8, v);
+  }
+}
+
+template <typename T>
+static hipError_t rmsnorm_t(const void* x, bool x_f32, int ldx, float* res_copy,
+                            const void* gain, void* out, bool out_f32, int rows, int H,
+                            float eps, hipStream_t s) {
+  const T* g = static_cast<const T*>(gain);
+  dim3 grid(rows), block(256);
+  if (x_f32 && out_f32)
+    rmsnorm_kernel<float, T, float><<<grid, block, 0, s>>>(static_cast<const float*>(x), ldx,
+                                                           res_copy, g,
+                                                           static_cast<float*>(out), H, eps);
+  else if (x_f32)
+    rmsnorm_kernel<float, T, T><<<grid, block, 0, s>>>(static_cast<const float*>(x), ldx,
+                                                       res_copy, g, static_cast<T*>(out), H,
+                                                       eps);
+  else if (out_f32)
+    rmsnorm_kernel<T, T, float><<<grid, block, 0, s>>>(static_cast<const T*>(x), ldx, res_copy,
+                                                       g, static_cast<float*>(out), H, eps);
+  else
+    rmsnorm_kernel<T, T, T><<<grid, block, 0, s>>>(static_cast<const T*>(x), ldx, res_copy, g,
+                                                   static_cast<T*>(out), H, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(Act act, const void* x, bool x_f32, int ldx, float* res_copy,
+                          const void* gain, void* out, bool out_f32, int rows, int H,
+                          float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (act == Act::F32)
+    return rmsnorm_t<float>(x, x_f32, ldx, res_copy, gain, out, out_f32, rows, H, eps, s);
+  return rmsnorm_t<uint16_t>(x, x_f32, ldx, res_copy, gain, out, out_f32, rows, H, eps, s);
+}
+
+// One block per token; wave w walks heads w, w+4, ... of [Q heads | K heads | V heads].
+// Lane i owns the rotate-half pair (i, i + hd/2) of a Q/K head, so the head's
+// RMSNorm is a single wavefront reduction and RoPE needs no data exchange.
+template <typename T>
+__global__ __launch_bounds__(256) void qk_rope_store_kernel(
+    T* __restrict__ qkv, int qkv_ld, const T* __restrict__ q_gain,
+    const T* __restrict__ k_gain, int qk_norm, float eps, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, T* __restrict__ k_layer, T* __restrict__ v_layer,
+    int max_seq, int start, int nq, int nkv, int hd) {
+  const int t = blockIdx.x;
+  const int pos = start + t;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = hd >> 1;
+  T* row = qkv + static_cast<size_t>(t) * qkv_ld;
+  const int n_heads = nq + 2 * nkv;
+  for (int hh = wave; hh < n_heads; hh += 4) {
+    T* src = row + hh * hd;
+    if (hh >= nq + nkv) {  // V head: raw copy into the cache slot
+      const int j = hh - nq - nkv;
+      T* dst = v_layer + (static_cast<size_t>(j) * max_seq + pos) * hd;
+      for (int i = lane; i < hd; i += 64) dst[i] = src[i];
+      continue;
+    }
+    const bool active = lane < half;
+    float x1 = 0.f, x2 = 0.f;
+    if (active) {
+      x1 = to_f32(src[lane]);
+      x2 = to_f32(src[lane + half]);
+    }
+    if (qk_norm) {
+      const float ss = wave_sum(x1 * x1 + x2 * x2);
+      const float inv = rsqrtf(ss / static_cast<float>(hd) + eps);
+      const T* g = hh < nq ? q_gain : k_gain;
+      if (active) {
+        x1 = to_f32(g[lane]) * (x1 * inv);
+        x2 = to_f32(g[lane + half]) * (x2 * inv);
+      }
+    }
+    if (!active) continue;
+    const float c = rope_cos[static_cast<size_t>(pos) * half + lane];
+    const float sn = rope_sin[static_cast<size_t>(pos) * half + lane];
+    const float y1 = x1 * c - x2 * sn;
+    const float y2 = x2 * c + x1 * sn;
+    T* dst = hh < nq ? src : k_layer + (static_cast<size_t>(hh - nq) * max_seq + pos) * hd;
+    dst[lane] = from_f32<T>(y1);
+    dst[lane + half] = from_f32<T>(y2);
+  }
+}
+
+hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const void* q_gain,
+                                const void* k_gain, bool qk_norm, float eps,
+                                const float* rope_cos, const float* rope_sin, void* k_layer,
+                                void* v_layer, int max_seq, int start, int nq, int nkv,
+                                int head_dim, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  dim3 grid(M), block(256);
+  if (act == Act::F32)
+    qk_rope_store_kernel<float><<<grid, block, 0, s>>>(
+        static_cast<float*>(qkv), qkv_ld, static_cast<const float*>(q_gain),
+        static_cast<const float*>(k_gain), qk_norm ? 1 : 0, eps, rope_cos, rope_sin,
+        static_cast<float*>(k_layer), static_cast<float*>(v_layer), max_seq, start, nq, nkv,
+        head_dim);
+  else
+    qk_rope_store_kernel<uint16_t><<<grid, block, 0, s>>>(
+        static_cast<uint16_t*>(qkv), qkv_ld, static_cast<const uint16_t*>(q_gain),
+        static_cast<const uint16_t*>(k_gain), qk_norm ? 1 : 0, eps, rope_cos, rope_sin,
+        static_cast<uint16_t*>(k_layer), static_cast<uint16_t*>(v_layer), max_seq, start, nq,
+        nkv, head_dim);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void store_rows_kernel(const float* __restrict__ src,
+                                                         T* __restrict__ dst, size_t n8) {
+  for (size_t c = blockIdx.x * 256ull + threadIdx.x; c < n8; c += gridDim.x * 256ull) {
+    float v[8];
+    load8(src + c * 8, v);
+    store8(dst + c * 8, v);
+  }
+}
+
+hipError_t launch_store_rows(Act act, const float* src, void* dst, int rows, int H,
+                             hipStream_t s) {
+  const size_t n8 = static_cast<size_t>(rows) * H / 8;
+  if (n8 == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(n8 / 256 + 1 < 4096 ? n8 / 256 + 1 : 4096);
+  if (act == Act::F32)
+    store_rows_kernel<float><<<blocks, 256, 0, s>>>(src, static_cast<float*>(dst), n8);
+  else
+    store_rows_kernel<uint16_t><<<blocks, 256, 0, s>>>(src, static_cast<uint16_t*>(dst), n8);
+  return hipGetLastError();
+}
+
+// LM head: each wavefront owns whole rows of W; a lane streams 16-byte chunks
+// of the row and the dot product ends in one wavefront reduction.  HBM-bound:
+// the weight is read exactly once.
+template <typename T>
+__global__ __launch_bounds__(256) void lm_head_kernel(const float* __restrict__ xn,
+                                                      const T* __restrict__ W,
+                                                      float* __restrict__ logits, int V, int H) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  const int chunks = H >> 3;
+  for (int r = gw; r < V; r += nw) {
+    const T* wr = W + static_cast<size_t>(r) * H;
+    float acc = 0.f;
+    for (int c = lane; c < chunks; c += 64) {
+      float w[8], x[8];
+      load8(wr + c * 8, w);
+      load8(xn + c * 8, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += w[i] * x[i];
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) logits[r] = acc;
+  }
+}
+
+hipError_t launch_lm_head(Act act, const float* xn, const void* W, float* logits, int V, int H,
+                          hipStream_t s) {
+  if (V <= 0) return hipSuccess;
+  const int blocks = (V + 3) / 4 < 8192 ? (V + 3) / 4 : 8192;
+  if (act == Act::F32)
+    lm_head_kernel<float><<<blocks, 256, 0, s>>>(xn, static_cast<const float*>(W), logits, V, H);
+  else
+    lm_head_kernel<uint16_t><<<blocks, 256, 0, s>>>(xn, static_cast<const uint16_t*>(W), logits,
+                                                    V, H);
+  return hipGetLastError();
+}
+
+}  // namespace tlp
