@@ -102,11 +102,11 @@ typedef struct {
 } tlp_layer_weights;
 
 /* Workspace regions (for tlp_workspace_layout).  After tlp_prefill_layer they
- * hold that call's intermediates: RES fp32 [n][H] residual stream after the
- * output projection; XN the FFN-normed rows [n][H] (dtype); QKV [n][(nq+2nkv)hd]
- * with Q normed and roped in place (dtype); ATTN [n][nq*hd] attention output
- * (dtype); ACT [n][I] SwiGLU output (dtype); HEAD fp32 [H] normed last row
- * (chunk only). */
+ * hold that call's intermediates: RES fp32 [n][H] the residual stream, i.e.
+ * the layer's output before it is rounded to dtype; XN the FFN-normed rows
+ * [n][H] (dtype); QKV [n][(nq+2nkv)hd] (dtype) with Q normed and roped in place
+ * and K, V as projected; ATTN [n][nq*hd] attention output (dtype); ACT [n][I]
+ * SwiGLU output (dtype); HEAD fp32 [H] normed last row (chunk with a head). */
 enum { TLP_WS_RES = 0, TLP_WS_XN = 1, TLP_WS_QKV = 2, TLP_WS_ATTN = 3, TLP_WS_ACT = 4,
        TLP_WS_HEAD = 5, TLP_WS_COUNT = 6 };
 

@@ -82,6 +82,13 @@ class GpuRun:
     def host(self, t):
         return self.tensors.to_host(t)
 
+    def residual_rows(self, n):
+        """fp32 residual stream [n][H] left in the workspace by the last call."""
+        off = self.tlp.workspace_layout(self.cfg, n)[self.tlp.WS_RES]
+        H = self.shape.hidden
+        raw = self.ws[off:off + n * H * 4]
+        return raw.view(self.torch.float32).reshape(n, H).cpu().numpy().astype(np.float64)
+
 
 def widen_caches(shape, kc, vc):
     return synth.widen(kc, shape.dtype), synth.widen(vc, shape.dtype)

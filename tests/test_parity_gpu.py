@@ -3,7 +3,10 @@
 Tolerance: infinity-norm relative error <= 2e-2 for bf16 inputs with fp32
 accumulation and <= 1e-4 for the fp32 path, on the output hidden rows, on the
 layer delta (output - input, so the residual cannot hide an error), on the
-K/V cache slots written and on the logits.  Cache-slot indexing is checked
+K/V cache slots written and on the logits.  The delta is taken from the fp32
+residual stream the library leaves in its workspace: the bf16 hidden output is
+rounded to 8 significant bits, and one rounding step of a residual of size ~4
+is already a few percent of a delta of size ~0.3.  Cache-slot indexing is checked
 bit-exactly: exactly the slots [start, start + n) of the layer change.
 
 Small shapes run the whole oracle; the full-size workloads compare sampled
@@ -38,6 +41,7 @@ def _check_layer(shape, rows=None, layer=0, label=""):
     gpu.layer(layer, sh.n_tokens, sh.start)
     g_hidden = synth.widen(gpu.host(gpu.hidden), sh.dtype)
     g_kc, g_vc = gpu.host(gpu.kc), gpu.host(gpu.vc)
+    g_res = gpu.residual_rows(sh.n_tokens)
     out, kc64, vc64 = oracle_layer(sh, w, layer, x, kc, vc, rows=rows)
     x64 = synth.widen(x, sh.dtype)
     sel = slice(None) if rows is None else rows
@@ -45,7 +49,7 @@ def _check_layer(shape, rows=None, layer=0, label=""):
     n, s = sh.n_tokens, sh.start
     errs = {
         "hidden": rel_err(g_hidden[sel], out),
-        "delta": rel_err(g_hidden[sel] - x64[sel], out - x64[sel]),
+        "delta": rel_err(g_res[sel] - x64[sel], out - x64[sel]),
         "k_slots": rel_err(synth.widen(g_kc[layer, :, s:s + n], sh.dtype), kc64[layer, :, s:s + n]),
         "v_slots": rel_err(synth.widen(g_vc[layer, :, s:s + n], sh.dtype), vc64[layer, :, s:s + n]),
     }
@@ -154,7 +158,11 @@ def test_chunk_matches_oracle_and_is_chunking_invariant():
         g = synth.widen(gpu.host(gpu.hidden), sh.dtype)
         g_kc, g_vc = gpu.host(gpu.kc), gpu.host(gpu.vc)
         e_h = rel_err(g, ref)
-        e_d = rel_err(g - synth.widen(x, sh.dtype), ref - synth.widen(x, sh.dtype))
+        # delta of the whole stack on the last micro-batch, from the fp32 stream
+        last = (sh.n_tokens - 1) // mb * mb
+        res = gpu.residual_rows(min(sh.n_tokens, mb))[:sh.n_tokens - last]
+        x64 = synth.widen(x, sh.dtype)
+        e_d = rel_err(res - x64[last:], ref[last:] - x64[last:])
         e_l = rel_err(logits.cpu().numpy(), ref_logits)
         e_k = rel_err(synth.widen(g_kc[:, :, sh.start:sh.start + sh.n_tokens], sh.dtype),
                       kc64[:, :, sh.start:sh.start + sh.n_tokens])

@@ -260,6 +260,7 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   if (out_act) {
     g.out = out_act;
     g.out_f32 = act == Act::F32;
+    g.res_out = res;   // the layer's output also stays in the fp32 residual stream
   } else {
     g.out = res;
     g.out_f32 = true;

@@ -20,6 +20,7 @@ struct GemmArgs {
   const uint16_t* Wscale;  // fp16 bit patterns
   void* out;
   const float* resid;
+  float* res_out;
   int lda, ldo, ldr;
   int M, N, K;
   int m_tiles, n_tiles;
@@ -221,7 +222,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
           const int n = nt * BN + wn * TN + j * 32 + lr;
           if (n >= g.N) continue;
           float v = acc[i][j][r];
-          if constexpr (EPI == 1) v += g.resid[static_cast<size_t>(m) * g.ldr + n];
+          if constexpr (EPI == 1) {
+            v += g.resid[static_cast<size_t>(m) * g.ldr + n];
+            if (g.res_out) g.res_out[static_cast<size_t>(m) * g.ldr + n] = v;
+          }
           if constexpr (OUT_F32)
             static_cast<float*>(g.out)[static_cast<size_t>(m) * g.ldo + n] = v;
           else
@@ -299,7 +303,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
         const int n = nt * BN + cols[j];
         if (n >= g.N) continue;
         float v = acc[i][j];
-        if (EPI == 1) v += g.resid[static_cast<size_t>(m) * g.ldr + n];
+        if (EPI == 1) {
+          v += g.resid[static_cast<size_t>(m) * g.ldr + n];
+          if (g.res_out) g.res_out[static_cast<size_t>(m) * g.ldr + n] = v;
+        }
         static_cast<float*>(g.out)[static_cast<size_t>(m) * g.ldo + n] = v;
       }
     }
@@ -340,6 +347,7 @@ hipError_t launch_gemm(const GemmCall& c, hipStream_t s) {
   g.Wscale = static_cast<const uint16_t*>(c.Wscale);
   g.out = c.out;
   g.resid = c.resid;
+  g.res_out = c.res_out;
   g.lda = c.lda;
   g.ldo = c.ldo;
   g.ldr = c.ldr;

@@ -33,6 +33,7 @@ struct GemmCall {
   bool out_f32;
   const float* resid;  // Resid: fp32 [M][ldr] added to the product (may alias out)
   int ldr;
+  float* res_out;      // Resid, optional: fp32 copy of the sum, row stride ldr (may alias resid)
 };
 hipError_t launch_gemm(const GemmCall& c, hipStream_t s);
 
