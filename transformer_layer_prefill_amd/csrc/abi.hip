@@ -237,7 +237,11 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g.A = attn; g.lda = qd;
   g.W = w.w_o.data; g.Wscale = w.w_o.scales;
   g.M = n; g.N = H; g.K = qd;
-  g.epi = Epi::Resid; g.out = res; g.ldo = H; g.out_f32 = true; g.resid = res; g.ldr = H;
+  if (act == Act::BF16) {
+    g.epi = Epi::AtomicAdd; g.out = res; g.ldo = H; g.out_f32 = true;
+  } else {
+    g.epi = Epi::Resid; g.out = res; g.ldo = H; g.out_f32 = true; g.resid = res; g.ldr = H;
+  }
   TLP_LAUNCH(TLP_K_O_GEMM, launch_gemm(g, s));
   // 5. FFN RMSNorm
   TLP_LAUNCH(TLP_K_FFN_NORM, launch_rmsnorm(act, res, true, H, nullptr, w.ffn_norm, xn, false, n, H, c.rms_eps,
@@ -256,16 +260,23 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g.A = a; g.lda = I;
   g.W = w.w_down.data; g.Wscale = w.w_down.scales;
   g.M = n; g.N = H; g.K = I;
-  g.epi = Epi::Resid; g.resid = res; g.ldr = H; g.ldo = H;
-  if (out_act) {
-    g.out = out_act;
-    g.out_f32 = act == Act::F32;
-    g.res_out = res;   // the layer's output also stays in the fp32 residual stream
+  if (act == Act::BF16) {
+    // split-K atomic adds into the fp32 stream, then one rounding pass to dtype
+    g.epi = Epi::AtomicAdd; g.out = res; g.ldo = H; g.out_f32 = true;
+    TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm(g, s));
+    if (out_act) TLP_LAUNCH(TLP_K_STORE_ROWS, launch_store_rows(act, res, out_act, n, H, s));
   } else {
-    g.out = res;
-    g.out_f32 = true;
+    g.epi = Epi::Resid; g.resid = res; g.ldr = H; g.ldo = H;
+    if (out_act) {
+      g.out = out_act;
+      g.out_f32 = true;
+      g.res_out = res;   // the layer's output also stays in the fp32 residual stream
+    } else {
+      g.out = res;
+      g.out_f32 = true;
+    }
+    TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm(g, s));
   }
-  TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm(g, s));
   return TLP_OK;
 }
 

@@ -24,8 +24,16 @@ struct GemmArgs {
   int lda, ldo, ldr;
   int M, N, K;
   int m_tiles, n_tiles;
+  int splits, k_split;  // split-K: number of K slices and K per slice (multiple of 64)
   int up_row;  // SwiGLU: row offset of the up half (= N)
 };
+
+// v if ok, else zero.  Done per component: a select between two uint4
+// aggregates compiles to a round trip through scratch memory.
+__device__ __forceinline__ uint4 keep_if(uint4 v, bool ok) {
+  const uint32_t m = ok ? 0xffffffffu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
@@ -37,6 +45,51 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 __device__ __forceinline__ int xcd_tile(int b, int nb) {
   if ((nb & 7) != 0) return b;
   return (b & 7) * (nb >> 3) + (b >> 3);
+}
+
+// Epilogue shared by the bf16 kernels.  32x32 accumulator layout: lane owns
+// column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
+template <int FM, int FN, int TM, int TN, int BN, int EPI, bool OUT_F32>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16_t (&acc)[FM][FN], int m0,
+                                              int nt, int wm, int wn, int lr, int lh) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * TM + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+      if (m >= g.M) continue;
+      if constexpr (EPI == 2) {
+        uint16_t* o = static_cast<uint16_t*>(g.out) + static_cast<size_t>(m) * g.ldo;
+#pragma unroll
+        for (int j = 0; j < FN / 2; ++j) {
+          const int n = nt * (BN / 2) + wn * (TN / 2) + j * 32 + lr;
+          if (n < g.N) {
+            const float gate = acc[i][j][r], up = acc[i][j + FN / 2][r];
+            o[n] = f32_to_bf16(silu_f32(gate) * up);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int n = nt * BN + wn * TN + j * 32 + lr;
+          if (n >= g.N) continue;
+          float v = acc[i][j][r];
+          if constexpr (EPI == 3) {
+            unsafeAtomicAdd(static_cast<float*>(g.out) + static_cast<size_t>(m) * g.ldo + n, v);
+            continue;
+          }
+          if constexpr (EPI == 1) {
+            v += g.resid[static_cast<size_t>(m) * g.ldr + n];
+            if (g.res_out) g.res_out[static_cast<size_t>(m) * g.ldr + n] = v;
+          }
+          if constexpr (OUT_F32)
+            static_cast<float*>(g.out)[static_cast<size_t>(m) * g.ldo + n] = v;
+          else
+            static_cast<uint16_t*>(g.out)[static_cast<size_t>(m) * g.ldo + n] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool SIGN1, bool OUT_F32>
@@ -57,11 +110,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LD];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LD];
 
-  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  // work item -> (split, M-tile, N-tile); the K slices of one tile and the
+  // M-tiles of one weight tile stay on one XCD
+  const int wi = xcd_tile(blockIdx.x, gridDim.x);
+  const int split = wi % g.splits, t = wi / g.splits;
   const int mt = t % g.m_tiles, nt = t / g.m_tiles;
   const int m0 = mt * BM;
+  const int k_begin = split * g.k_split;
+  const int k_end = min(g.K, k_begin + g.k_split);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 31, lh = lane >> 5;
 
   // weight row of LDS tile row r (SwiGLU interleaves gate and up halves per wave)
   auto b_row = [&](int r, bool& ok) -> int {
@@ -77,63 +136,69 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     }
   };
 
+  // Chunk i of a thread is tile row tid/8 + i*T/8 at column (tid%8)*8.  Rows
+  // outside the matrix and columns past the K slice read a clamped in-bounds
+  // address and are zeroed, so the loads never branch.
+  const int kc = (tid & 7) * 8;
+  const int r0 = tid >> 3;
+  const uint16_t* Wd = static_cast<const uint16_t*>(g.W);
+  const uint32_t* Wb = static_cast<const uint32_t*>(g.W);
+
   uint4 a_reg[A_PER];
   uint4 b_reg[SIGN1 ? 1 : B_PER];
   uint32_t s_word[SIGN1 ? S_PER : 1];
   uint16_t s_scale[SIGN1 ? S_PER : 1];
 
-  auto load_tiles = [&](int k0) {
+  // Validity of the chunks in flight; applied when they are written to LDS so
+  // the wait for the global loads falls after the MFMAs of the current tile.
+  bool a_ok[A_PER], b_ok[SIGN1 ? 1 : B_PER], s_ok[SIGN1 ? S_PER : 1];
+
+  auto load_tiles = [&](int k0) __attribute__((always_inline)) {
+    const bool k_ok = k0 + kc < k_end;
+    const int col = k_ok ? k0 + kc : 0;   // invalid chunks read column 0 of their row
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      const int c = tid + i * T;
-      const int r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-      const int m = m0 + r, k = k0 + kc;
-      a_reg[i] = (m < g.M && k < g.K)
-                     ? *reinterpret_cast<const uint4*>(g.A + static_cast<size_t>(m) * g.lda + k)
-                     : make_uint4(0, 0, 0, 0);
+      const int m = m0 + r0 + i * (T / 8);
+      a_ok[i] = m < g.M && k_ok;
+      a_reg[i] = *reinterpret_cast<const uint4*>(
+          g.A + static_cast<size_t>(m < g.M ? m : g.M - 1) * g.lda + col);
     }
     if constexpr (!SIGN1) {
-      const uint16_t* W = static_cast<const uint16_t*>(g.W);
 #pragma unroll
       for (int i = 0; i < B_PER; ++i) {
-        const int c = tid + i * T;
-        const int r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
         bool ok;
-        const int n = b_row(r, ok);
-        const int k = k0 + kc;
-        b_reg[i] = (ok && k < g.K)
-                       ? *reinterpret_cast<const uint4*>(W + static_cast<size_t>(n) * g.K + k)
-                       : make_uint4(0, 0, 0, 0);
+        const int n = b_row(r0 + i * (T / 8), ok);
+        b_ok[i] = ok && k_ok;
+        b_reg[i] = *reinterpret_cast<const uint4*>(
+            Wd + static_cast<size_t>(ok ? n : 0) * g.K + col);
       }
     } else {
-      const uint32_t* Wb = static_cast<const uint32_t*>(g.W);
 #pragma unroll
       for (int i = 0; i < S_PER; ++i) {
         const int c = tid + i * T;
-        const int r = c >> 1, wd = c & 1;
         bool ok;
-        const int n = b_row(r, ok);
-        const int k = k0 + wd * 32;
-        ok = ok && k < g.K;
-        s_word[i] = ok ? Wb[static_cast<size_t>(n) * (g.K >> 5) + (k >> 5)] : 0u;
-        s_scale[i] = ok ? g.Wscale[static_cast<size_t>(n) * (g.K >> 7) + (k >> 7)] : 0;
+        const int n = b_row(c >> 1, ok);
+        const int k = k0 + (c & 1) * 32;
+        ok = ok && k < k_end;
+        const size_t row = static_cast<size_t>(ok ? n : 0);
+        s_ok[i] = ok;
+        s_word[i] = Wb[row * (g.K >> 5) + (ok ? (k >> 5) : 0)];
+        s_scale[i] = g.Wscale[row * (g.K >> 7) + (ok ? (k >> 7) : 0)];
       }
     }
   };
 
-  auto store_tiles = [&](int buf) {
+  auto store_tiles = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      const int c = tid + i * T;
-      const int r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-      *reinterpret_cast<uint4*>(&As[buf][r * LD + kc]) = a_reg[i];
+      const int r = r0 + i * (T / 8);
+      *reinterpret_cast<uint4*>(&As[buf][r * LD + kc]) = keep_if(a_reg[i], a_ok[i]);
     }
     if constexpr (!SIGN1) {
 #pragma unroll
       for (int i = 0; i < B_PER; ++i) {
-        const int c = tid + i * T;
-        const int r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-        *reinterpret_cast<uint4*>(&Bs[buf][r * LD + kc]) = b_reg[i];
+        const int r = r0 + i * (T / 8);
+        *reinterpret_cast<uint4*>(&Bs[buf][r * LD + kc]) = keep_if(b_reg[i], b_ok[i]);
       }
     } else {
 #pragma unroll
@@ -141,8 +206,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
         const int c = tid + i * T;
         const int r = c >> 1, wd = c & 1;
         // +scale for a set bit, -scale for a clear one, as bf16 bit patterns
-        const uint32_t pos = f32_to_bf16(f16_to_f32(s_scale[i]));
-        const uint32_t neg = pos | 0x8000u;
+        const uint32_t pos = s_ok[i] ? f32_to_bf16(f16_to_f32(s_scale[i])) : 0u;
+        const uint32_t neg = s_ok[i] ? (pos | 0x8000u) : 0u;
         const uint32_t w = s_word[i];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -168,72 +233,185 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (g.K + BK - 1) / BK;
-  load_tiles(0);
+  // Fragment registers are double-buffered across the four 16-wide k-steps of
+  // a tile, so the LDS reads of step kk+1 are in flight during step kk's MFMAs.
+  bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
+#define TLP_LOAD_FRAGS(AF, BF, BUF, KK)                                                  \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                 \
+      *reinterpret_cast<const bf16x8_t*>(&As[BUF][(wm * TM + i * 32 + lr) * LD + (KK) * 16 + lh * 8]); \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) BF[j] =                                 \
+      *reinterpret_cast<const bf16x8_t*>(&Bs[BUF][(wn * TN + j * 32 + lr) * LD + (KK) * 16 + lh * 8]);
+#define TLP_MMA(AF, BF)                                                                  \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i)                                         \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j)                                         \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AF[i], BF[j], acc[i][j], 0, 0, 0);
+
+  const int nk = (k_end - k_begin + BK - 1) / BK;
+  load_tiles(k_begin);
   store_tiles(0);
   __syncthreads();
+  TLP_LOAD_FRAGS(af0, bf0, 0, 0)
 
-  const int lr = lane & 31, lh = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load_tiles((kt + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(
-            &As[buf][(wm * TM + i * 32 + lr) * LD + kk * 16 + lh * 8]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(
-            &Bs[buf][(wn * TN + j * 32 + lr) * LD + kk * 16 + lh * 8]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_tiles(buf ^ 1);
+    const bool more = kt + 1 < nk;
+    if (more) load_tiles(k_begin + (kt + 1) * BK);
+    TLP_LOAD_FRAGS(af1, bf1, buf, 1)
+    TLP_MMA(af0, bf0)
+    TLP_LOAD_FRAGS(af0, bf0, buf, 2)
+    TLP_MMA(af1, bf1)
+    TLP_LOAD_FRAGS(af1, bf1, buf, 3)
+    TLP_MMA(af0, bf0)
+    // the next tile goes into the other buffer, whose last reads (k-step 3 of
+    // the previous tile) completed before the previous barrier
+    if (more) store_tiles(buf ^ 1);
     __syncthreads();
+    if (more) { TLP_LOAD_FRAGS(af0, bf0, buf ^ 1, 0) }
+    TLP_MMA(af1, bf1)
+  }
+#undef TLP_LOAD_FRAGS
+#undef TLP_MMA
+
+  gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh);
+}
+
+// ---- bf16 kernel with direct global->LDS loads ------------------------------
+// Dense weights with K a multiple of 32.  Tiles are 32 wide in K and staged
+// through a 4-deep LDS ring filled by global_load_lds_dwordx4 (no register
+// staging), so three tiles are in flight while one is multiplied.  Each DMA
+// instruction writes 1 KB (16 rows of 64 B) contiguously; lane l of it fetches
+// the 16-byte chunk (l%4) ^ swz(row) of row l/4, which stores chunk c of row r
+// at slot c ^ swz(r) and keeps the fragment reads free of bank conflicts.
+// Rows past M or N are clamped to a valid row; their products land in
+// discarded outputs.
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// s_waitcnt immediate that waits for vmcnt <= n and nothing else (GFX9 layout)
+template <int N>
+struct VmWait {
+  static constexpr int imm = (N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14);
+};
+
+// 16-byte global -> LDS copy per lane; `lds` must be the same for the whole
+// wavefront (it becomes M0), lane l lands at lds + 16 * l.
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) {
+  constexpr int BK = 32, S = 4;
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;  // DMA blocks per wave
+  constexpr int LOADS = A_PW + B_PW;                                       // per wave per tile
+  static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "DMA split");
+  static_assert(EPI != 2 || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+
+  const int wi = xcd_tile(blockIdx.x, gridDim.x);
+  const int split = wi % g.splits, t = wi / g.splits;
+  const int mt = t % g.m_tiles, nt = t / g.m_tiles;
+  const int m0 = mt * BM;
+  const int k_begin = split * g.k_split;
+  const int k_end = min(g.K, k_begin + g.k_split);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 31, lh = lane >> 5;
+  const uint16_t* W = static_cast<const uint16_t*>(g.W);
+
+  // global source rows of this lane's DMA chunks (fixed over the K loop)
+  const int drow = lane >> 2, dslot = lane & 3;
+  const uint16_t* a_src[A_PW];
+  const uint16_t* b_src[B_PW];
+#pragma unroll
+  for (int j = 0; j < A_PW; ++j) {
+    const int row = (wave * A_PW + j) * 16 + drow;
+    const int m = min(m0 + row, g.M - 1);
+    a_src[j] = g.A + static_cast<size_t>(m) * g.lda + (dslot ^ swz4(row)) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < B_PW; ++j) {
+    const int row = (wave * B_PW + j) * 16 + drow;
+    int n;
+    if constexpr (EPI == 2) {
+      const int w = row / TN, rr = row % TN;
+      const int jj = min(nt * (BN / 2) + w * (TN / 2) + rr % (TN / 2), g.N - 1);
+      n = rr >= TN / 2 ? g.up_row + jj : jj;
+    } else {
+      n = min(nt * BN + row, g.N - 1);
+    }
+    b_src[j] = W + static_cast<size_t>(n) * g.K + (dslot ^ swz4(row)) * 8;
   }
 
-  // Epilogue.  32x32 accumulator layout: lane owns column (lane & 31) and rows
-  // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = k_begin + kt * BK;
+    char* st = smem + (kt % S) * STAGE;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int j = 0; j < A_PW; ++j) dma16(a_src[j] + k0, st + (wave * A_PW + j) * 1024);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * TM + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-      if (m >= g.M) continue;
-      if constexpr (EPI == 2) {
-        uint16_t* o = static_cast<uint16_t*>(g.out) + static_cast<size_t>(m) * g.ldo;
+    for (int j = 0; j < B_PW; ++j) dma16(b_src[j] + k0, st + A_BYTES + (wave * B_PW + j) * 1024);
+  };
+
+  f32x16_t acc[FM][FN];
 #pragma unroll
-        for (int j = 0; j < FN / 2; ++j) {
-          const int n = nt * (BN / 2) + wn * (TN / 2) + j * 32 + lr;
-          if (n < g.N) {
-            const float gate = acc[i][j][r], up = acc[i][j + FN / 2][r];
-            o[n] = f32_to_bf16(silu_f32(gate) * up);
-          }
-        }
-      } else {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int n = nt * BN + wn * TN + j * 32 + lr;
-          if (n >= g.N) continue;
-          float v = acc[i][j][r];
-          if constexpr (EPI == 1) {
-            v += g.resid[static_cast<size_t>(m) * g.ldr + n];
-            if (g.res_out) g.res_out[static_cast<size_t>(m) * g.ldr + n] = v;
-          }
-          if constexpr (OUT_F32)
-            static_cast<float*>(g.out)[static_cast<size_t>(m) * g.ldo + n] = v;
-          else
-            static_cast<uint16_t*>(g.out)[static_cast<size_t>(m) * g.ldo + n] = f32_to_bf16(v);
-        }
-      }
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fragment byte offsets inside a stage: row base*64 + swizzled chunk
+  const int sw = swz4(lr);
+  const int a_off = (wm * TM + lr) * 64, b_off = A_BYTES + (wn * TN + lr) * 64;
+  const int c0 = ((0 * 2 + lh) ^ sw) << 4, c1 = ((1 * 2 + lh) ^ sw) << 4;
+  bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
+
+  const int nk = (k_end - k_begin) / BK;
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < nk) issue(p);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // tile kt has landed once at most (tiles issued after it) * LOADS remain
+    const int after = min(S - 2, nk - 1 - kt);
+    if (after >= 2) __builtin_amdgcn_s_waitcnt(VmWait<2 * LOADS>::imm);
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(VmWait<LOADS>::imm);
+    else __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+    // barrier without the full memory fence of __syncthreads, which would also
+    // wait for the DMA loads of the tiles still in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // refill the stage every wave finished multiplying in the previous iteration
+    if (kt + S - 1 < nk) issue(kt + S - 1);
+    const char* st = smem + (kt % S) * STAGE;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      af0[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 32 * 64 + c0);
+      af1[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 32 * 64 + c1);
     }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      bf0[j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * 64 + c0);
+      bf1[j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * 64 + c1);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af0[i], bf0[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j], acc[i][j], 0, 0, 0);
   }
+
+  gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh);
 }
 
 // ---- fp32 FMA kernel --------------------------------------------------------
@@ -314,18 +492,45 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool SIGN1, bool OUT_F32>
-static hipError_t run_bf16(GemmArgs g, hipStream_t s) {
+static hipError_t run_bf16(GemmArgs g, int splits, hipStream_t s) {
   const int cols = EPI == 2 ? BN / 2 : BN;
   g.m_tiles = (g.M + BM - 1) / BM;
   g.n_tiles = (g.N + cols - 1) / cols;
-  const int blocks = g.m_tiles * g.n_tiles;
+  // the direct-to-LDS kernel needs whole 32-wide K tiles; it slices K by 32
+  const bool dma = !SIGN1 && g.K % 32 == 0;
+  const int kt_w = dma ? 32 : 64;
+  const int k_tiles = (g.K + kt_w - 1) / kt_w;
+  if (splits > k_tiles) splits = k_tiles;
+  if (splits < 1) splits = 1;
+  const int per = (k_tiles + splits - 1) / splits;   // K tiles per slice
+  g.k_split = per * kt_w;
+  g.splits = (k_tiles + per - 1) / per;
+  const int blocks = g.m_tiles * g.n_tiles * g.splits;
+  if (dma) {
+    gemm_bf16_dma_kernel<BM, BN, WM, WN, EPI, OUT_F32><<<blocks, WM * WN * 64, 0, s>>>(g);
+    return hipGetLastError();
+  }
   gemm_bf16_kernel<BM, BN, WM, WN, EPI, SIGN1, OUT_F32><<<blocks, WM * WN * 64, 0, s>>>(g);
   return hipGetLastError();
 }
 
+// Tile shape per call.  Large weight matrices take 256x256 tiles (128x128 per
+// wavefront, the LDS traffic per MFMA is half that of 64x64 wavefront tiles);
+// shapes with too few such tiles to fill the 256 CUs fall back to 128x128.
+// The atomic-add epilogue (fp32 residual stream) splits K until the grid has
+// about one work item per CU.
+constexpr int kCUs = 256;
+
 template <int EPI, bool SIGN1, bool OUT_F32>
 static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
-  return run_bf16<128, 128, 2, 2, EPI, SIGN1, OUT_F32>(g, s);
+  const int cols_big = EPI == 2 ? 128 : 256;
+  const long tiles_big = static_cast<long>((g.M + 255) / 256) * ((g.N + cols_big - 1) / cols_big);
+  if (EPI == 3) {
+    const int splits = static_cast<int>((kCUs + tiles_big - 1) / tiles_big);
+    return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, splits, s);
+  }
+  if (tiles_big >= kCUs * 3 / 4) return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, 1, s);
+  return run_bf16<128, 128, 2, 2, EPI, SIGN1, OUT_F32>(g, 1, s);
 }
 
 template <bool SIGN1>
@@ -333,6 +538,7 @@ static hipError_t dispatch_bf16(const GemmCall& c, GemmArgs g, hipStream_t s) {
   switch (c.epi) {
     case Epi::Store: return pick_bf16<0, SIGN1, false>(g, s);
     case Epi::SwiGLU: return pick_bf16<2, SIGN1, false>(g, s);
+    case Epi::AtomicAdd: return pick_bf16<3, SIGN1, true>(g, s);
     case Epi::Resid:
       return c.out_f32 ? pick_bf16<1, SIGN1, true>(g, s) : pick_bf16<1, SIGN1, false>(g, s);
   }
@@ -364,6 +570,7 @@ hipError_t launch_gemm(const GemmCall& c, hipStream_t s) {
       case Epi::Store: gemm_f32_kernel<0><<<blocks, 256, 0, s>>>(g); break;
       case Epi::Resid: gemm_f32_kernel<1><<<blocks, 256, 0, s>>>(g); break;
       case Epi::SwiGLU: gemm_f32_kernel<2><<<blocks, 256, 0, s>>>(g); break;
+      case Epi::AtomicAdd: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }

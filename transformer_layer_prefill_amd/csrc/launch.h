@@ -19,7 +19,10 @@ hipError_t launch_rmsnorm(Act act, const void* x, bool x_f32, int ldx, float* re
                           float eps, hipStream_t s);
 
 // ---- projection GEMM: C[m][n] = sum_k A[m][k] * W[n][k] ---------------------
-enum class Epi { Store = 0, Resid = 1, SwiGLU = 2 };
+// Store: out = A W^T (act type).  Resid: out = resid + A W^T.  SwiGLU: out[:, j] =
+// silu(gate_j) * up_j with gate rows [0, N) and up rows [N, 2N) of W.
+// AtomicAdd: fp32 out += A W^T with atomic adds (bf16 only; may split K).
+enum class Epi { Store = 0, Resid = 1, SwiGLU = 2, AtomicAdd = 3 };
 struct GemmCall {
   Act act;             // A, W (dense) and Store/SwiGLU outputs use this type
   const void* A;       // [M][K], row stride lda
