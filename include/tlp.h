@@ -66,7 +66,7 @@ typedef enum { TLP_F32 = 0, TLP_BF16 = 1 } tlp_dtype;
 typedef enum { TLP_W_DENSE = 0, TLP_W_SIGN1_G128 = 1 } tlp_wformat;
 
 typedef struct {
-  int32_t hidden;       /* H; multiple of 8 */
+  int32_t hidden;       /* H; multiple of 8, at most 16384 */
   int32_t intermediate; /* I; multiple of 8 */
   int32_t n_q_heads;    /* nq; multiple of n_kv_heads */
   int32_t n_kv_heads;   /* nkv; nq/nkv in {1, 2, 4} or a multiple of 4 */
@@ -106,9 +106,10 @@ typedef struct {
  * the layer's output before it is rounded to dtype; XN the FFN-normed rows
  * [n][H] (dtype); QKV [n][(nq+2nkv)hd] (dtype) with Q normed and roped in place
  * and K, V as projected; ATTN [n][nq*hd] attention output (dtype); ACT [n][I]
- * SwiGLU output (dtype); HEAD fp32 [H] normed last row (chunk with a head). */
+ * SwiGLU output (dtype); HEAD fp32 [H] normed last row (chunk with a head);
+ * PART fp32 split-K slices of the output and down projections (bf16 only). */
 enum { TLP_WS_RES = 0, TLP_WS_XN = 1, TLP_WS_QKV = 2, TLP_WS_ATTN = 3, TLP_WS_ACT = 4,
-       TLP_WS_HEAD = 5, TLP_WS_COUNT = 6 };
+       TLP_WS_HEAD = 5, TLP_WS_PART = 6, TLP_WS_COUNT = 7 };
 
 /* Bytes of workspace a call with up to `max_tokens` tokens per micro-batch
  * needs (tlp_prefill_chunk: max_tokens = min(n_tokens, micro_batch)).
@@ -171,7 +172,7 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
 /* Kernels as timed by the profiler below. */
 enum { TLP_K_ATTN_NORM = 0, TLP_K_QKV_GEMM = 1, TLP_K_QK_ROPE_KV = 2, TLP_K_ATTENTION = 3,
        TLP_K_O_GEMM = 4, TLP_K_FFN_NORM = 5, TLP_K_GATE_UP_GEMM = 6, TLP_K_DOWN_GEMM = 7,
-       TLP_K_FINAL_NORM = 8, TLP_K_LM_HEAD = 9, TLP_K_STORE_ROWS = 10, TLP_K_COUNT = 11 };
+       TLP_K_FINAL_NORM = 8, TLP_K_LM_HEAD = 9, TLP_K_OUT_ROWS = 10, TLP_K_COUNT = 11 };
 
 /* Per-kernel GPU timing, the analog of the per-layer / per-command-buffer
  * profiling switches of the pages (metal_full_layer.rs OXIBONSAI_PROFILE and

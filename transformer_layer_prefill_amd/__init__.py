@@ -6,7 +6,7 @@ supplies device memory and streams.  Build the library with
 """
 from ._lib import (EXPORTS, KERNELS, LIB_PATH, TLP_BF16, TLP_ERR_HIP, TLP_ERR_NULL, TLP_ERR_POSITION,
                    TLP_ERR_SHAPE, TLP_ERR_UNSUPPORTED, TLP_ERR_WORKSPACE, TLP_F32, TLP_OK,
-                   TLP_W_DENSE, TLP_W_SIGN1_G128, WS_ACT, WS_ATTN, WS_COUNT, WS_HEAD, WS_QKV,
+                   TLP_W_DENSE, TLP_W_SIGN1_G128, WS_ACT, WS_ATTN, WS_COUNT, WS_HEAD, WS_PART, WS_QKV,
                    WS_RES, WS_XN, Config, LayerWeights, TlpError, Weight, lib, make_config,
                    prefill_chunk, prefill_layer, profile_begin, profile_end, rope_table, workspace_bytes, workspace_layout)
 
@@ -15,4 +15,4 @@ __all__ = ["EXPORTS", "KERNELS", "LIB_PATH", "profile_begin", "profile_end", "Co
            "workspace_layout", "TLP_OK", "TLP_ERR_NULL", "TLP_ERR_SHAPE", "TLP_ERR_POSITION",
            "TLP_ERR_UNSUPPORTED", "TLP_ERR_WORKSPACE", "TLP_ERR_HIP", "TLP_F32", "TLP_BF16",
            "TLP_W_DENSE", "TLP_W_SIGN1_G128", "WS_RES", "WS_XN", "WS_QKV", "WS_ATTN", "WS_ACT",
-           "WS_HEAD", "WS_COUNT"]
+           "WS_HEAD", "WS_PART", "WS_COUNT"]

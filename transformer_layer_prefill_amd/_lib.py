@@ -17,13 +17,13 @@ TLP_OK, TLP_ERR_NULL, TLP_ERR_SHAPE, TLP_ERR_POSITION = 0, 1, 2, 3
 TLP_ERR_UNSUPPORTED, TLP_ERR_WORKSPACE, TLP_ERR_HIP = 4, 5, 6
 TLP_F32, TLP_BF16 = 0, 1
 TLP_W_DENSE, TLP_W_SIGN1_G128 = 0, 1
-WS_RES, WS_XN, WS_QKV, WS_ATTN, WS_ACT, WS_HEAD, WS_COUNT = range(7)
+WS_RES, WS_XN, WS_QKV, WS_ATTN, WS_ACT, WS_HEAD, WS_PART, WS_COUNT = range(8)
 
 EXPORTS = ("tlp_workspace_bytes", "tlp_workspace_layout", "tlp_rope_table",
            "tlp_prefill_layer", "tlp_prefill_chunk", "tlp_profile_begin", "tlp_profile_end",
            "tlp_status_string", "tlp_last_error")
 KERNELS = ("attn_norm", "qkv_gemm", "qk_rope_kv", "attention", "o_gemm", "ffn_norm",
-           "gate_up_gemm", "down_gemm", "final_norm", "lm_head", "store_rows")
+           "gate_up_gemm", "down_gemm", "final_norm", "lm_head", "out_rows")
 
 
 class TlpError(RuntimeError):

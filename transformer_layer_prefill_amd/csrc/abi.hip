@@ -49,6 +49,8 @@ tlp_status check_config(const tlp_config* c) {
   if (c->hidden <= 0 || c->intermediate <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
       c->max_seq <= 0 || c->n_layers <= 0)
     return fail(TLP_ERR_SHAPE, "sizes must be positive");
+  if (c->hidden > 16384)
+    return fail(TLP_ERR_UNSUPPORTED, "hidden %d above 16384", c->hidden);
   if (c->hidden % 8 || c->intermediate % 8)
     return fail(TLP_ERR_SHAPE, "hidden (%d) and intermediate (%d) must be multiples of 8",
                 c->hidden, c->intermediate);
@@ -69,6 +71,20 @@ tlp_status check_config(const tlp_config* c) {
   return TLP_OK;
 }
 
+// Rows of split-K slices (slices x micro-batch rows) the output and down
+// projections may write for any micro-batch of at most m rows (bf16 path).
+size_t part_rows(const tlp_config& c, int m) {
+  if (c.dtype != TLP_BF16) return 0;
+  size_t best = 0;
+  for (int r = 1; r <= m; ++r) {
+    const int a = tlp::gemm_partial_splits(r, c.hidden, c.n_q_heads * c.head_dim);
+    const int b = tlp::gemm_partial_splits(r, c.hidden, c.intermediate);
+    const size_t rows = static_cast<size_t>(a > b ? a : b) * r;
+    if (rows > best) best = rows;
+  }
+  return best;
+}
+
 struct Layout {
   size_t off[TLP_WS_COUNT];
   size_t total;
@@ -84,6 +100,7 @@ Layout layout_of(const tlp_config& c, int m) {
       M * static_cast<size_t>(c.n_q_heads) * c.head_dim * e,  // ATTN
       M * c.intermediate * e,                                 // ACT
       static_cast<size_t>(c.hidden) * 4,                      // HEAD
+      part_rows(c, m) * c.hidden * 4,                          // PART
   };
   Layout L{};
   size_t o = 0;
@@ -190,20 +207,24 @@ struct ProfScope {
       return fail(TLP_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_));           \
   } while (0)
 
-// One layer over the rows already in the workspace / hidden.  x_in: the rows'
-// input (hidden in act type when x_in_f32 is false, else the fp32 residual
-// stream); out_act: when non-null the down projection writes dtype rows there,
-// otherwise it updates the fp32 residual stream in place.
+// One layer over a micro-batch.  x_in holds the rows' input: the hidden rows
+// in the activation type (x_in_f32 false) or the fp32 residual stream, to which
+// the in_parts split-K slices of the previous layer's down projection are
+// added.  out_act non-null: the layer's output is also rounded into out_act
+// (and *out_parts = 0); otherwise the down projection's slices are left for
+// the next layer (*out_parts = their count; the fp32 path never splits).
 tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer, int n,
-                     int start, const void* x_in, bool x_in_f32, void* out_act, char* kc,
-                     char* vc, const float* cs, const float* sn, char* ws, const Layout& L,
-                     hipStream_t s) {
+                     int start, const void* x_in, bool x_in_f32, int in_parts, void* out_act,
+                     int* out_parts, char* kc, char* vc, const float* cs, const float* sn,
+                     char* ws, const Layout& L, hipStream_t s) {
   using namespace tlp;
   const Act act = c.dtype == TLP_F32 ? Act::F32 : Act::BF16;
   const int H = c.hidden, I = c.intermediate, hd = c.head_dim;
   const int nq = c.n_q_heads, nkv = c.n_kv_heads;
   const int qkv_dim = (nq + 2 * nkv) * hd, qd = nq * hd;
   float* res = reinterpret_cast<float*>(ws + L.off[TLP_WS_RES]);
+  float* part = reinterpret_cast<float*>(ws + L.off[TLP_WS_PART]);
+  const size_t part_stride = static_cast<size_t>(n) * H;
   void* xn = ws + L.off[TLP_WS_XN];
   void* qkv = ws + L.off[TLP_WS_QKV];
   void* attn = ws + L.off[TLP_WS_ATTN];
@@ -212,10 +233,16 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   const size_t layer_off = static_cast<size_t>(layer) * nkv * c.max_seq * hd * es;
   void* k_layer = kc + layer_off;
   void* v_layer = vc + layer_off;
+  const bool split = act == Act::BF16;
 
-  // 1. attention RMSNorm (fp32 copy of the input rows becomes the residual stream)
-  TLP_LAUNCH(TLP_K_ATTN_NORM, launch_rmsnorm(act, x_in, x_in_f32, H, x_in_f32 ? nullptr : res, w.attn_norm, xn,
-                            false, n, H, c.rms_eps, s));
+  // 1. residual assembly + attention RMSNorm
+  RowArgs r{};
+  r.x = x_in; r.x_f32 = x_in_f32; r.ldx = H;
+  r.part = part; r.n_part = in_parts; r.part_stride = part_stride;
+  r.res_out = res;
+  r.gain = w.attn_norm; r.norm_out = xn;
+  r.rows = n; r.H = H; r.eps = c.rms_eps;
+  TLP_LAUNCH(TLP_K_ATTN_NORM, launch_rownorm(act, r, s));
   // 2. fused QKV projection
   GemmCall g{};
   g.act = act;
@@ -231,21 +258,28 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   // 3e. causal GQA attention
   TLP_LAUNCH(TLP_K_ATTENTION, launch_attention(act, qkv, qkv_dim, k_layer, v_layer, attn, qd, n, start, nq, nkv,
                               hd, c.max_seq, s));
-  // 4. output projection + residual (fp32 stream, in place)
+  // 4. output projection: split-K slices (bf16) or a fused residual add (fp32)
+  int o_parts = 0;
   g = GemmCall{};
   g.act = act;
   g.A = attn; g.lda = qd;
   g.W = w.w_o.data; g.Wscale = w.w_o.scales;
   g.M = n; g.N = H; g.K = qd;
-  if (act == Act::BF16) {
-    g.epi = Epi::AtomicAdd; g.out = res; g.ldo = H; g.out_f32 = true;
+  if (split) {
+    g.epi = Epi::Partial; g.out = part; g.ldo = H; g.out_f32 = true;
+    g.part_stride = part_stride; g.splits_out = &o_parts;
   } else {
     g.epi = Epi::Resid; g.out = res; g.ldo = H; g.out_f32 = true; g.resid = res; g.ldr = H;
   }
   TLP_LAUNCH(TLP_K_O_GEMM, launch_gemm(g, s));
-  // 5. FFN RMSNorm
-  TLP_LAUNCH(TLP_K_FFN_NORM, launch_rmsnorm(act, res, true, H, nullptr, w.ffn_norm, xn, false, n, H, c.rms_eps,
-                            s));
+  // 5. residual assembly + FFN RMSNorm
+  r = RowArgs{};
+  r.x = res; r.x_f32 = 1; r.ldx = H;
+  r.part = part; r.n_part = o_parts; r.part_stride = part_stride;
+  r.res_out = res;
+  r.gain = w.ffn_norm; r.norm_out = xn;
+  r.rows = n; r.H = H; r.eps = c.rms_eps;
+  TLP_LAUNCH(TLP_K_FFN_NORM, launch_rownorm(act, r, s));
   // 6. gate/up projection + SwiGLU
   g = GemmCall{};
   g.act = act;
@@ -254,28 +288,35 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g.M = n; g.N = I; g.K = H;
   g.epi = Epi::SwiGLU; g.out = a; g.ldo = I;
   TLP_LAUNCH(TLP_K_GATE_UP_GEMM, launch_gemm(g, s));
-  // 7. down projection + residual
+  // 7. down projection
+  int d_parts = 0;
   g = GemmCall{};
   g.act = act;
   g.A = a; g.lda = I;
   g.W = w.w_down.data; g.Wscale = w.w_down.scales;
   g.M = n; g.N = H; g.K = I;
-  if (act == Act::BF16) {
-    // split-K atomic adds into the fp32 stream, then one rounding pass to dtype
-    g.epi = Epi::AtomicAdd; g.out = res; g.ldo = H; g.out_f32 = true;
-    TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm(g, s));
-    if (out_act) TLP_LAUNCH(TLP_K_STORE_ROWS, launch_store_rows(act, res, out_act, n, H, s));
+  if (split) {
+    g.epi = Epi::Partial; g.out = part; g.ldo = H; g.out_f32 = true;
+    g.part_stride = part_stride; g.splits_out = &d_parts;
   } else {
-    g.epi = Epi::Resid; g.resid = res; g.ldr = H; g.ldo = H;
+    g.epi = Epi::Resid; g.resid = res; g.ldr = H; g.ldo = H; g.out_f32 = true;
+    g.out = out_act ? out_act : res;
+    if (out_act) g.res_out = res;   // the output also stays in the fp32 stream
+  }
+  TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm(g, s));
+  *out_parts = 0;
+  if (split) {
     if (out_act) {
-      g.out = out_act;
-      g.out_f32 = true;
-      g.res_out = res;   // the layer's output also stays in the fp32 residual stream
+      // residual assembly into the fp32 stream and the activation-type output
+      r = RowArgs{};
+      r.x = res; r.x_f32 = 1; r.ldx = H;
+      r.part = part; r.n_part = d_parts; r.part_stride = part_stride;
+      r.res_out = res; r.act_out = out_act; r.ld_act = H;
+      r.rows = n; r.H = H; r.eps = c.rms_eps;
+      TLP_LAUNCH(TLP_K_OUT_ROWS, launch_rownorm(act, r, s));
     } else {
-      g.out = res;
-      g.out_f32 = true;
+      *out_parts = d_parts;
     }
-    TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm(g, s));
   }
   return TLP_OK;
 }
@@ -333,9 +374,10 @@ tlp_status tlp_prefill_layer(const tlp_config* cfg, const tlp_layer_weights* wei
   const Layout L = layout_of(*cfg, n_tokens);
   hipStream_t st = static_cast<hipStream_t>(stream);
   g_last_error.clear();
-  return run_layer(*cfg, *weights, layer, n_tokens, start_position, hidden, false, hidden,
-                   static_cast<char*>(k_cache), static_cast<char*>(v_cache), rope_cos, rope_sin,
-                   static_cast<char*>(workspace), L, st);
+  int parts = 0;
+  return run_layer(*cfg, *weights, layer, n_tokens, start_position, hidden, false, 0, hidden,
+                   &parts, static_cast<char*>(k_cache), static_cast<char*>(v_cache), rope_cos,
+                   rope_sin, static_cast<char*>(workspace), L, st);
 }
 
 tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* layers,
@@ -373,11 +415,12 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
   for (int off = 0; off < n_tokens; off += mb) {
     const int m = n_tokens - off < mb ? n_tokens - off : mb;
     char* rows = static_cast<char*>(hidden) + static_cast<size_t>(off) * row_bytes;
+    int parts = 0;
     for (int l = 0; l < cfg->n_layers; ++l) {
       const bool first = l == 0, last = l == cfg->n_layers - 1;
       s = run_layer(*cfg, layers[l], l, m, start_position + off,
                     first ? static_cast<const void*>(rows) : ws + L.off[TLP_WS_RES], !first,
-                    last ? rows : nullptr, static_cast<char*>(k_cache),
+                    parts, last ? rows : nullptr, &parts, static_cast<char*>(k_cache),
                     static_cast<char*>(v_cache), rope_cos, rope_sin, ws, L, st);
       if (s != TLP_OK) return s;
     }
@@ -386,8 +429,11 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
     hipStream_t s = st;
     const char* last_row = static_cast<char*>(hidden) + static_cast<size_t>(n_tokens - 1) * row_bytes;
     float* xh = reinterpret_cast<float*>(ws + L.off[TLP_WS_HEAD]);
-    TLP_LAUNCH(TLP_K_FINAL_NORM, launch_rmsnorm(act, last_row, false, cfg->hidden, nullptr, final_norm, xh, true, 1,
-                              cfg->hidden, final_eps, st));
+    RowArgs r{};
+    r.x = last_row; r.x_f32 = 0; r.ldx = cfg->hidden;
+    r.gain = final_norm; r.norm_out = xh; r.norm_f32 = 1;
+    r.rows = 1; r.H = cfg->hidden; r.eps = final_eps;
+    TLP_LAUNCH(TLP_K_FINAL_NORM, launch_rownorm(act, r, s));
     TLP_LAUNCH(TLP_K_LM_HEAD, launch_lm_head(act, xh, lm_head, logits, vocab, cfg->hidden, s));
   }
   return TLP_OK;

@@ -25,6 +25,8 @@ struct GemmArgs {
   int M, N, K;
   int m_tiles, n_tiles;
   int splits, k_split;  // split-K: number of K slices and K per slice (multiple of 64)
+  size_t part_stride;   // Partial epilogue: elements between K-slice outputs
+  int* splits_out;      // host-side only: receives the K slice count
   int up_row;  // SwiGLU: row offset of the up half (= N)
 };
 
@@ -51,7 +53,7 @@ __device__ __forceinline__ int xcd_tile(int b, int nb) {
 // column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
 template <int FM, int FN, int TM, int TN, int BN, int EPI, bool OUT_F32>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16_t (&acc)[FM][FN], int m0,
-                                              int nt, int wm, int wn, int lr, int lh) {
+                                              int nt, int wm, int wn, int lr, int lh, int split) {
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -74,8 +76,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16_t (&acc)
           const int n = nt * BN + wn * TN + j * 32 + lr;
           if (n >= g.N) continue;
           float v = acc[i][j][r];
-          if constexpr (EPI == 3) {
-            unsafeAtomicAdd(static_cast<float*>(g.out) + static_cast<size_t>(m) * g.ldo + n, v);
+          if constexpr (EPI == 4) {
+            static_cast<float*>(g.out)[split * g.part_stride + static_cast<size_t>(m) * g.ldo + n] = v;
             continue;
           }
           if constexpr (EPI == 1) {
@@ -272,13 +274,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 #undef TLP_LOAD_FRAGS
 #undef TLP_MMA
 
-  gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh);
+  gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh, split);
 }
 
 // ---- bf16 kernel with direct global->LDS loads ------------------------------
 // Dense weights with K a multiple of 32.  Tiles are 32 wide in K and staged
-// through a 4-deep LDS ring filled by global_load_lds_dwordx4 (no register
-// staging), so three tiles are in flight while one is multiplied.  Each DMA
+// through a 5-deep LDS ring (160 KB at 256x256) filled by
+// global_load_lds_dwordx4 (no register staging), so up to three tiles are in
+// flight while one is multiplied.  Each DMA
 // instruction writes 1 KB (16 rows of 64 B) contiguously; lane l of it fetches
 // the 16-byte chunk (l%4) ^ swz(row) of row l/4, which stores chunk c of row r
 // at slot c ^ swz(r) and keeps the fragment reads free of bank conflicts.
@@ -302,7 +305,7 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
 
 template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) {
-  constexpr int BK = 32, S = 4;
+  constexpr int BK = 32, S = 5;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
@@ -371,47 +374,69 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
   const int a_off = (wm * TM + lr) * 64, b_off = A_BYTES + (wn * TN + lr) * 64;
   const int c0 = ((0 * 2 + lh) ^ sw) << 4, c1 = ((1 * 2 + lh) ^ sw) << 4;
   bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
+#define TLP_FRAGS(AF, BF, ST, C)                                                             \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                     \
+      *reinterpret_cast<const bf16x8_t*>((ST) + a_off + i * 32 * 64 + (C));                  \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) BF[j] =                                     \
+      *reinterpret_cast<const bf16x8_t*>((ST) + b_off + j * 32 * 64 + (C));
+#define TLP_MMA(AF, BF)                                                                      \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i)                                             \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AF[i], BF[j], acc[i][j], 0, 0, 0);
 
+  // Schedule per 32-wide tile kt (two 16-wide k-steps):
+  //   read step-1 fragments of kt | MFMAs of step 0
+  //   wait for tile kt+1, barrier, refill the stage of tile kt-1,
+  //   read step-0 fragments of kt+1 | MFMAs of step 1
+  // so LDS reads always overlap MFMAs and the barrier sits between MFMA blocks.
   const int nk = (k_end - k_begin) / BK;
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
     if (p < nk) issue(p);
+  // tile 0 has landed once the tiles issued after it are all that remain
+  if (nk > S - 2) __builtin_amdgcn_s_waitcnt(VmWait<(S - 2) * LOADS>::imm);
+  else __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  TLP_FRAGS(af0, bf0, smem, c0)
+  // drain every scalar load too: a scalar load still pending at the loop
+  // entry would force full LDS waits inside the loop
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // tile kt has landed once at most (tiles issued after it) * LOADS remain
-    const int after = min(S - 2, nk - 1 - kt);
-    if (after >= 2) __builtin_amdgcn_s_waitcnt(VmWait<2 * LOADS>::imm);
-    else if (after == 1) __builtin_amdgcn_s_waitcnt(VmWait<LOADS>::imm);
+  // Main loop: every iteration has a next tile, so the LDS reads are the same
+  // on every path and the compiler's wait counting stays exact.
+  int kt = 0;
+  for (; kt + 1 < nk; ++kt) {
+    const char* st = smem + (kt % S) * STAGE;
+    TLP_FRAGS(af1, bf1, st, c1)
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af0, bf0)
+    __builtin_amdgcn_sched_barrier(0);
+    // tiles issued so far end at kt+S-2; tile kt+1 has landed once at most the
+    // (up to S-3) tiles after it are still in flight
+    if (kt + S - 2 < nk) __builtin_amdgcn_s_waitcnt(VmWait<(S - 3) * LOADS>::imm);
     else __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
     // barrier without the full memory fence of __syncthreads, which would also
     // wait for the DMA loads of the tiles still in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // refill the stage every wave finished multiplying in the previous iteration
+    // every wave has read all of tile kt-1: its stage takes tile kt+S-1
     if (kt + S - 1 < nk) issue(kt + S - 1);
-    const char* st = smem + (kt % S) * STAGE;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      af0[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 32 * 64 + c0);
-      af1[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 32 * 64 + c1);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      bf0[j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * 64 + c0);
-      bf1[j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * 64 + c1);
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af0[i], bf0[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j], acc[i][j], 0, 0, 0);
+    const char* st1 = smem + ((kt + 1) % S) * STAGE;
+    TLP_FRAGS(af0, bf0, st1, c0)
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af1, bf1)
+    __builtin_amdgcn_sched_barrier(0);
   }
+  {
+    const char* st = smem + (kt % S) * STAGE;
+    TLP_FRAGS(af1, bf1, st, c1)
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af0, bf0)
+    TLP_MMA(af1, bf1)
+  }
+#undef TLP_FRAGS
+#undef TLP_MMA
 
-  gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh);
+  gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh, split);
 }
 
 // ---- fp32 FMA kernel --------------------------------------------------------
@@ -506,6 +531,7 @@ static hipError_t run_bf16(GemmArgs g, int splits, hipStream_t s) {
   g.k_split = per * kt_w;
   g.splits = (k_tiles + per - 1) / per;
   const int blocks = g.m_tiles * g.n_tiles * g.splits;
+  if (g.splits_out) *g.splits_out = g.splits;
   if (dma) {
     gemm_bf16_dma_kernel<BM, BN, WM, WN, EPI, OUT_F32><<<blocks, WM * WN * 64, 0, s>>>(g);
     return hipGetLastError();
@@ -514,20 +540,31 @@ static hipError_t run_bf16(GemmArgs g, int splits, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile shape per call.  Large weight matrices take 256x256 tiles (128x128 per
-// wavefront, the LDS traffic per MFMA is half that of 64x64 wavefront tiles);
-// shapes with too few such tiles to fill the 256 CUs fall back to 128x128.
-// The atomic-add epilogue (fp32 residual stream) splits K until the grid has
-// about one work item per CU.
+// Tile shape per call.  Large weight matrices take 256x256 tiles; shapes with
+// too few such tiles to fill the 256 CUs fall back to 128x128.  The Partial
+// epilogue (output projection and down projection, summed later by the row
+// pass that consumes the residual stream) splits K until the grid has about
+// one work item per CU, at most 8 slices.
 constexpr int kCUs = 256;
+constexpr int kMaxSplits = 8;
+
+static int big_tiles(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+
+int gemm_partial_splits(int M, int N, int K) {
+  const int tiles = big_tiles(M, N);
+  int splits = (kCUs + tiles - 1) / tiles;
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  const int k_tiles = (K + 31) / 32;
+  if (splits > k_tiles) splits = k_tiles;
+  return splits < 1 ? 1 : splits;
+}
 
 template <int EPI, bool SIGN1, bool OUT_F32>
 static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
   const int cols_big = EPI == 2 ? 128 : 256;
   const long tiles_big = static_cast<long>((g.M + 255) / 256) * ((g.N + cols_big - 1) / cols_big);
-  if (EPI == 3) {
-    const int splits = static_cast<int>((kCUs + tiles_big - 1) / tiles_big);
-    return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, splits, s);
+  if (EPI == 4) {
+    return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, gemm_partial_splits(g.M, g.N, g.K), s);
   }
   if (tiles_big >= kCUs * 3 / 4) return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, 1, s);
   return run_bf16<128, 128, 2, 2, EPI, SIGN1, OUT_F32>(g, 1, s);
@@ -538,7 +575,7 @@ static hipError_t dispatch_bf16(const GemmCall& c, GemmArgs g, hipStream_t s) {
   switch (c.epi) {
     case Epi::Store: return pick_bf16<0, SIGN1, false>(g, s);
     case Epi::SwiGLU: return pick_bf16<2, SIGN1, false>(g, s);
-    case Epi::AtomicAdd: return pick_bf16<3, SIGN1, true>(g, s);
+    case Epi::Partial: return pick_bf16<4, SIGN1, true>(g, s);
     case Epi::Resid:
       return c.out_f32 ? pick_bf16<1, SIGN1, true>(g, s) : pick_bf16<1, SIGN1, false>(g, s);
   }
@@ -554,6 +591,8 @@ hipError_t launch_gemm(const GemmCall& c, hipStream_t s) {
   g.out = c.out;
   g.resid = c.resid;
   g.res_out = c.res_out;
+  g.part_stride = c.part_stride;
+  g.splits_out = c.splits_out;
   g.lda = c.lda;
   g.ldo = c.ldo;
   g.ldr = c.ldr;
@@ -570,7 +609,7 @@ hipError_t launch_gemm(const GemmCall& c, hipStream_t s) {
       case Epi::Store: gemm_f32_kernel<0><<<blocks, 256, 0, s>>>(g); break;
       case Epi::Resid: gemm_f32_kernel<1><<<blocks, 256, 0, s>>>(g); break;
       case Epi::SwiGLU: gemm_f32_kernel<2><<<blocks, 256, 0, s>>>(g); break;
-      case Epi::AtomicAdd: return hipErrorInvalidValue;
+      case Epi::Partial: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }

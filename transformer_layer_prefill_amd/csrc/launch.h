@@ -10,19 +10,32 @@ namespace tlp {
 
 enum class Act { F32 = 0, BF16 = 1 };
 
-// ---- RMSNorm over rows ------------------------------------------------------
-// out[r][:] = gain * x[r][:] / sqrt(mean(x[r]^2) + eps) for r < rows.
-// x_f32 selects the input type (fp32 residual stream or activation type);
-// res_copy (nullable) receives x as fp32, the layer's residual stream.
-hipError_t launch_rmsnorm(Act act, const void* x, bool x_f32, int ldx, float* res_copy,
-                          const void* gain, void* out, bool out_f32, int rows, int H,
-                          float eps, hipStream_t s);
+// ---- residual assembly + RMSNorm over rows -----------------------------------
+// Row r: sum = x[r] + sum_p part[p][r]; optionally res_out[r] = sum (fp32),
+// act_out[r] = sum (activation type), norm_out[r] = gain * sum / sqrt(mean(sum^2) + eps).
+struct RowArgs {
+  const void* x;        // [rows][ldx], fp32 (x_f32) or activation type
+  int x_f32, ldx;
+  const float* part;    // [n_part][rows][H] split-K partial sums (nullable when n_part == 0)
+  int n_part;
+  size_t part_stride;   // elements between partial slices
+  float* res_out;       // nullable, [rows][H]
+  void* act_out;        // nullable, [rows][ld_act] activation type
+  int ld_act;
+  const void* gain;     // nullable (no norm), [H] activation type
+  void* norm_out;       // [rows][H], fp32 (norm_f32) or activation type
+  int norm_f32;
+  int rows, H;
+  float eps;
+};
+hipError_t launch_rownorm(Act act, const RowArgs& a, hipStream_t s);
 
 // ---- projection GEMM: C[m][n] = sum_k A[m][k] * W[n][k] ---------------------
 // Store: out = A W^T (act type).  Resid: out = resid + A W^T.  SwiGLU: out[:, j] =
 // silu(gate_j) * up_j with gate rows [0, N) and up rows [N, 2N) of W.
-// AtomicAdd: fp32 out += A W^T with atomic adds (bf16 only; may split K).
-enum class Epi { Store = 0, Resid = 1, SwiGLU = 2, AtomicAdd = 3 };
+// Partial: K is split into `splits` slices; slice s writes its fp32 product to
+// part + s * part_stride (row stride ldo) for a later row pass to sum (bf16 only).
+enum class Epi { Store = 0, Resid = 1, SwiGLU = 2, Partial = 4 };
 struct GemmCall {
   Act act;             // A, W (dense) and Store/SwiGLU outputs use this type
   const void* A;       // [M][K], row stride lda
@@ -37,8 +50,13 @@ struct GemmCall {
   const float* resid;  // Resid: fp32 [M][ldr] added to the product (may alias out)
   int ldr;
   float* res_out;      // Resid, optional: fp32 copy of the sum, row stride ldr (may alias resid)
+  size_t part_stride;  // Partial: elements between K-slice outputs (out is fp32)
+  int* splits_out;     // Partial, optional: receives the number of K slices written
 };
 hipError_t launch_gemm(const GemmCall& c, hipStream_t s);
+
+// K slices the Partial epilogue uses for an M x N x K bf16 product (1 if not split).
+int gemm_partial_splits(int M, int N, int K);
 
 // ---- QK-norm + RoPE + KV-cache store -----------------------------------------
 // Per token t (absolute position start + t): optional per-head RMSNorm of Q and K
@@ -62,8 +80,5 @@ hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_laye
 hipError_t launch_lm_head(Act act, const float* xn, const void* W, float* logits, int V, int H,
                           hipStream_t s);
 
-// Copy rows of the fp32 residual stream back to the activation type.
-hipError_t launch_store_rows(Act act, const float* src, void* dst, int rows, int H,
-                             hipStream_t s);
 
 }  // namespace tlp

@@ -40,68 +40,75 @@ __device__ __forceinline__ void store8(float* p, const float v[8]) {
   reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// One 256-thread block per row.  Pass 1 sums squares (fp32), pass 2 re-reads
-// the row (an L1/L2 hit) and writes gain * x * rsqrt(mean + eps).
-template <typename TX, typename TG, typename TO>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, int ldx,
-                                                      float* __restrict__ res_copy,
-                                                      const TG* __restrict__ gain,
-                                                      TO* __restrict__ out, int H, float eps) {
+// One 256-thread block per row.  The row is assembled once in registers:
+// x (activation type or fp32) plus the split-K partial sums of the projection
+// that produced it; the sum may be stored as the fp32 residual stream and/or
+// rounded to the activation type, and RMSNorm(sum) * gain is written when a
+// gain is given.  Up to 8 chunks of 8 elements per thread (H <= 16384).
+template <typename T, bool XF32, bool NORM_F32>
+__global__ __launch_bounds__(256) void rownorm_kernel(RowArgs a) {
+  constexpr int CH = 8;
   __shared__ float red[4];
   const int r = blockIdx.x;
-  const TX* xr = x + static_cast<size_t>(r) * ldx;
-  const int chunks = H >> 3;
+  const int chunks = a.H >> 3;
+  const size_t roff = static_cast<size_t>(r) * a.H;
+  float v[CH][8];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < chunks; c += 256) {
-    float v[8];
-    load8(xr + c * 8, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
-    if (res_copy) store8(res_copy + static_cast<size_t>(r) * H + c * 8, v);
+  for (int c = 0; c < CH; ++c) {
+    const int idx = threadIdx.x + c * 256;
+    if (idx >= chunks) break;
+    if constexpr (XF32)
+      load8(static_cast<const float*>(a.x) + static_cast<size_t>(r) * a.ldx + idx * 8, v[c]);
+    else
+      load8(static_cast<const T*>(a.x) + static_cast<size_t>(r) * a.ldx + idx * 8, v[c]);
+    for (int p = 0; p < a.n_part; ++p) {
+      float q[8];
+      load8(a.part + p * a.part_stride + roff + idx * 8, q);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[c][i] += q[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += v[c][i] * v[c][i];
+    if (a.res_out) store8(a.res_out + roff + idx * 8, v[c]);
+    if (a.act_out)
+      store8(static_cast<T*>(a.act_out) + static_cast<size_t>(r) * a.ld_act + idx * 8, v[c]);
   }
+  if (!a.gain) return;
   ss = block_sum<4>(ss, red);
-  const float inv = rsqrtf(ss / static_cast<float>(H) + eps);
-  TO* orow = out + static_cast<size_t>(r) * H;
-  for (int c = threadIdx.x; c < chunks; c += 256) {
-    float v[8], g[8];
-    load8(xr + c * 8, v);
-    load8(gain + c * 8, g);
+  const float inv = rsqrtf(ss / static_cast<float>(a.H) + a.eps);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = g[i] * (v[i] * inv);
-    store8(orow + c * 8, v);
+  for (int c = 0; c < CH; ++c) {
+    const int idx = threadIdx.x + c * 256;
+    if (idx >= chunks) break;
+    float g[8];
+    load8(static_cast<const T*>(a.gain) + idx * 8, g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[c][i] = g[i] * (v[c][i] * inv);
+    if constexpr (NORM_F32)
+      store8(static_cast<float*>(a.norm_out) + roff + idx * 8, v[c]);
+    else
+      store8(static_cast<T*>(a.norm_out) + roff + idx * 8, v[c]);
   }
 }
 
 template <typename T>
-static hipError_t rmsnorm_t(const void* x, bool x_f32, int ldx, float* res_copy,
-                            const void* gain, void* out, bool out_f32, int rows, int H,
-                            float eps, hipStream_t s) {
-  const T* g = static_cast<const T*>(gain);
-  dim3 grid(rows), block(256);
-  if (x_f32 && out_f32)
-    rmsnorm_kernel<float, T, float><<<grid, block, 0, s>>>(static_cast<const float*>(x), ldx,
-                                                           res_copy, g,
-                                                           static_cast<float*>(out), H, eps);
-  else if (x_f32)
-    rmsnorm_kernel<float, T, T><<<grid, block, 0, s>>>(static_cast<const float*>(x), ldx,
-                                                       res_copy, g, static_cast<T*>(out), H,
-                                                       eps);
-  else if (out_f32)
-    rmsnorm_kernel<T, T, float><<<grid, block, 0, s>>>(static_cast<const T*>(x), ldx, res_copy,
-                                                       g, static_cast<float*>(out), H, eps);
-  else
-    rmsnorm_kernel<T, T, T><<<grid, block, 0, s>>>(static_cast<const T*>(x), ldx, res_copy, g,
-                                                   static_cast<T*>(out), H, eps);
+static hipError_t rownorm_t(const RowArgs& a, hipStream_t s) {
+  dim3 grid(a.rows), block(256);
+  if (a.x_f32) {
+    if (a.norm_f32) rownorm_kernel<T, true, true><<<grid, block, 0, s>>>(a);
+    else rownorm_kernel<T, true, false><<<grid, block, 0, s>>>(a);
+  } else {
+    if (a.norm_f32) rownorm_kernel<T, false, true><<<grid, block, 0, s>>>(a);
+    else rownorm_kernel<T, false, false><<<grid, block, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(Act act, const void* x, bool x_f32, int ldx, float* res_copy,
-                          const void* gain, void* out, bool out_f32, int rows, int H,
-                          float eps, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  if (act == Act::F32)
-    return rmsnorm_t<float>(x, x_f32, ldx, res_copy, gain, out, out_f32, rows, H, eps, s);
-  return rmsnorm_t<uint16_t>(x, x_f32, ldx, res_copy, gain, out, out_f32, rows, H, eps, s);
+hipError_t launch_rownorm(Act act, const RowArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  if (a.H % 8 || a.H > 8 * 8 * 256) return hipErrorInvalidValue;
+  return act == Act::F32 ? rownorm_t<float>(a, s) : rownorm_t<uint16_t>(a, s);
 }
 
 // One block per token; wave w walks heads w, w+4, ... of [Q heads | K heads | V heads].
@@ -172,28 +179,6 @@ hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const voi
         static_cast<const uint16_t*>(k_gain), qk_norm ? 1 : 0, eps, rope_cos, rope_sin,
         static_cast<uint16_t*>(k_layer), static_cast<uint16_t*>(v_layer), max_seq, start, nq,
         nkv, head_dim);
-  return hipGetLastError();
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void store_rows_kernel(const float* __restrict__ src,
-                                                         T* __restrict__ dst, size_t n8) {
-  for (size_t c = blockIdx.x * 256ull + threadIdx.x; c < n8; c += gridDim.x * 256ull) {
-    float v[8];
-    load8(src + c * 8, v);
-    store8(dst + c * 8, v);
-  }
-}
-
-hipError_t launch_store_rows(Act act, const float* src, void* dst, int rows, int H,
-                             hipStream_t s) {
-  const size_t n8 = static_cast<size_t>(rows) * H / 8;
-  if (n8 == 0) return hipSuccess;
-  const unsigned blocks = static_cast<unsigned>(n8 / 256 + 1 < 4096 ? n8 / 256 + 1 : 4096);
-  if (act == Act::F32)
-    store_rows_kernel<float><<<blocks, 256, 0, s>>>(src, static_cast<float*>(dst), n8);
-  else
-    store_rows_kernel<uint16_t><<<blocks, 256, 0, s>>>(src, static_cast<uint16_t*>(dst), n8);
   return hipGetLastError();
 }
 
