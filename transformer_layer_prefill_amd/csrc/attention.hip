@@ -11,7 +11,7 @@
 // group.  Per 64-key block a wavefront computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (lane = query, 32 key scores per lane), runs the
 // online softmax in fp32 with exp2, and accumulates O^T = V^T P^T, taking P
-// straight from the score registers and V^T from a transposed LDS copy.
+// straight from the score registers and V^T from transposing LDS reads.
 #include "common.h"
 #include "launch.h"
 
@@ -30,15 +30,24 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(hd)
 };
 
+// K and V blocks of 64 keys are copied global -> LDS with DMA into a double
+// buffer (the next block streams in while the current one is multiplied).
+// Rows are stored as 16-byte chunks, chunk c of key row r at slot c ^ swz(r):
+// K uses r % 8 so the eight rows of a b128 fragment read hit distinct banks,
+// V uses 2 * (r % 4) so the four rows of a transposing read do.  Key rows past
+// the last visible key are clamped to it (finite data that the mask gives a
+// zero weight), so unwritten cache slots never reach the products.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a) {
-  constexpr int KB = 64;        // keys per block
-  constexpr int KLD = HD + 8;   // K row stride in LDS (elements)
-  constexpr int VLD = KB + 8;   // V^T row stride in LDS (elements)
-  constexpr int KS = HD / 16;   // k-steps of the QK^T contraction
-  constexpr int DB = HD / 32;   // 32-wide blocks of the head dimension
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * VLD];
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+  constexpr int KB = 64;                 // keys per block
+  constexpr int ROWB = HD * 2;           // bytes per key row
+  constexpr int CH = ROWB / 16;          // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROWB;       // rows per DMA instruction
+  constexpr int TILE = KB * ROWB;        // bytes of one K (or V) block
+  constexpr int PW = TILE / 1024 / 4;    // DMA instructions per wave per K (or V) block
+  constexpr int KS = HD / 16;            // k-steps of the QK^T contraction
+  constexpr int DB = HD / 32;            // 32-wide blocks of the head dimension
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];   // [buffer][K | V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lh = lane >> 5;
@@ -57,10 +66,11 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a) {
   bf16x8_t qf[KS];
   {
     const uint16_t* qrow = a.q + static_cast<size_t>(q_ok ? t : 0) * a.q_ld + h * HD;
+    const uint32_t keep = q_ok ? 0xffffffffu : 0u;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint4 u = q_ok ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + lh * 8)
-                     : make_uint4(0, 0, 0, 0);
+      uint4 u = *reinterpret_cast<const uint4*>(qrow + ks * 16 + lh * 8);
+      u = make_uint4(u.x & keep, u.y & keep, u.z & keep, u.w & keep);
       qf[ks] = __builtin_bit_cast(bf16x8_t, u);
     }
   }
@@ -71,6 +81,21 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a) {
   const uint16_t* kbase = a.k + static_cast<size_t>(j) * a.max_seq * HD;
   const uint16_t* vbase = a.v + static_cast<size_t>(j) * a.max_seq * HD;
 
+  // DMA: instruction q covers key rows q*RPI .. +RPI; lane -> (row, slot)
+  const int d_row = lane / CH, d_slot = lane % CH;
+  auto issue = [&](int kb) __attribute__((always_inline)) {
+    char* st = smem + (kb & 1) * 2 * TILE;
+#pragma unroll
+    for (int jj = 0; jj < PW; ++jj) {
+      const int q = wave * PW + jj;
+      const int row = q * RPI + d_row;
+      const int key = min(kb * KB + row, kv_end - 1);
+      dma16(kbase + static_cast<size_t>(key) * HD + (d_slot ^ (row & 7)) * 8, st + q * 1024);
+      dma16(vbase + static_cast<size_t>(key) * HD + (d_slot ^ ((row & 3) * 2)) * 8,
+            st + TILE + q * 1024);
+    }
+  };
+
   f32x16_t o[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d)
@@ -78,39 +103,20 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  // V^T transposing reads: lane group g = lane/16 covers head dims
+  // (g%2)*16 .. +16 of a 32-wide block for key half lh = g/2; source lane
+  // s = lane%16 points at key row (base + s/4), dims 4*(s%4) .. +4.
+  const int tr_key = (lane & 15) >> 2;                       // + key base
+  const int tr_dim = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;  // + 32*db
+
+  issue(0);
   for (int kb = 0; kb < nkb; ++kb) {
     const int key0 = kb * KB;
-    __syncthreads();
-    // stage K rows [key0, key0 + 64) and V^T; rows past kv_end are zero so an
-    // unwritten (possibly NaN) cache slot never reaches the products
-    for (int c = tid; c < KB * HD / 8; c += 256) {
-      const int row = c / (HD / 8), cc = (c % (HD / 8)) * 8;
-      const int key = key0 + row;
-      uint4 u = key < kv_end
-                    ? *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(key) * HD + cc)
-                    : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&Ks[row * KLD + cc]) = u;
-    }
-    for (int c = tid; c < (KB / 2) * (HD / 8); c += 256) {
-      const int kp = c % (KB / 2), dc = (c / (KB / 2)) * 8;
-      const int key = key0 + 2 * kp;
-      uint4 u0 = key < kv_end
-                     ? *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(key) * HD + dc)
-                     : make_uint4(0, 0, 0, 0);
-      uint4 u1 = key + 1 < kv_end ? *reinterpret_cast<const uint4*>(
-                                        vbase + static_cast<size_t>(key + 1) * HD + dc)
-                                  : make_uint4(0, 0, 0, 0);
-      const uint32_t w0[4] = {u0.x, u0.y, u0.z, u0.w};
-      const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint32_t*>(&Vt[(dc + 2 * e) * VLD + 2 * kp]) =
-            (w0[e] & 0xffffu) | (w1[e] << 16);
-        *reinterpret_cast<uint32_t*>(&Vt[(dc + 2 * e + 1) * VLD + 2 * kp]) =
-            (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-      }
-    }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wave's copies of block kb
+    lds_barrier();                                 // everyone's; buffer kb+1 is free
+    if (kb + 1 < nkb) issue(kb + 1);
+    const char* Kt = smem + (kb & 1) * 2 * TILE;
+    const char* Vt = Kt + TILE;
 
     // S^T for two 32-key halves: lane (query lr) gets keys 8*(r/4) + 4*lh + r%4
     f32x16_t s[2];
@@ -118,9 +124,11 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[hb][r] = 0.f;
+      const int krow = hb * 32 + lr;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[(hb * 32 + lr) * KLD + ks * 16 + lh * 8]);
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+            Kt + krow * ROWB + (((ks * 2 + lh) ^ (krow & 7)) << 4));
         s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[hb], 0, 0, 0);
       }
     }
@@ -155,15 +163,19 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
 
     // O^T += V^T P^T.  Slot (lh, e) of step (hb, half) is key
-    // hb*32 + half*16 + 8*(e/4) + 4*lh + e%4, matching the score layout above.
+    // hb*32 + half*16 + 8*(e/4) + 4*lh + e%4, matching the score layout above;
+    // each run of four consecutive keys is one transposing read.
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
-      const uint16_t* vrow = &Vt[(d * 32 + lr) * VLD];
+      const int dim = d * 32 + tr_dim;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const int base = (st >> 1) * 32 + (st & 1) * 16 + lh * 4;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + base);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + base + 8);
+        const int kbase_r = (st >> 1) * 32 + (st & 1) * 16 + lh * 4 + tr_key;
+        const int r0 = kbase_r, r1 = kbase_r + 8;
+        const uint2 lo = lds_read_tr16(Vt + r0 * ROWB + ((((dim >> 3)) ^ ((r0 & 3) * 2)) << 4) +
+                                       (dim & 7) * 2);
+        const uint2 hi = lds_read_tr16(Vt + r1 * ROWB + ((((dim >> 3)) ^ ((r1 & 3) * 2)) << 4) +
+                                       (dim & 7) * 2);
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], o[d], 0, 0, 0);
       }

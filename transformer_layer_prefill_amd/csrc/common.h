@@ -70,4 +70,39 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+// 16-byte global -> LDS copy per lane (global_load_lds_dwordx4); `lds` must be
+// the same for the whole wavefront (it becomes M0), lane l lands at lds + 16*l.
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
+// s_waitcnt immediate that waits for vmcnt <= n and nothing else (GFX9 layout)
+template <int N>
+struct VmWait {
+  static constexpr int imm = (N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14);
+};
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for every outstanding global->LDS copy); LDS reads issued before it
+// have completed.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane s supplies the address of 4 consecutive 16-bit values S[s][0..3]; lane i
+// of the group receives S[4e + i/4][i%4] for e = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)p);
+  return __builtin_bit_cast(uint2, v);
+#else
+  return make_uint2(0, 0);
+#endif
+}
+
 }  // namespace tlp

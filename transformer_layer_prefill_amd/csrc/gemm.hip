@@ -289,19 +289,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 // discarded outputs.
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
-// s_waitcnt immediate that waits for vmcnt <= n and nothing else (GFX9 layout)
-template <int N>
-struct VmWait {
-  static constexpr int imm = (N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14);
-};
-
-// 16-byte global -> LDS copy per lane; `lds` must be the same for the whole
-// wavefront (it becomes M0), lane l lands at lds + 16 * l.
-__device__ __forceinline__ void dma16(const void* src, void* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-#endif
-}
 
 template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) {
