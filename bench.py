@@ -77,6 +77,50 @@ def cpu_baseline(sh, w, x, kc, vc, budget_s=20.0):
                       f"({sh.n_tokens} tokens at start {sh.start}), mean {t:.3f} s each"}
 
 
+def csrc_sha256() -> str:
+    """Hash of the HIP sources; stored traffic counters only apply to this build."""
+    import hashlib
+    d = os.path.join(ROOT, "transformer_layer_prefill_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (scaled by the copy calibration), or None when they were
+    taken on other kernel sources or are absent."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != csrc_sha256():
+        return None
+    for name, v in t["kernels"].items():
+        if name.split(" | ")[0] == kernel:
+            return {"bytes": round(v["fetch_bytes"] + v["write_bytes"]),
+                    "fetch_bytes": round(v["fetch_bytes"]), "write_bytes": round(v["write_bytes"]),
+                    "source": f"profiles/traffic_{workload}.json"}
+    return None
+
+
+def copy_probe(mib: int) -> None:
+    """Copy mib MiB device-to-device five times: a kernel that reads and writes
+    exactly mib MiB each, against which FETCH_SIZE / WRITE_SIZE are scaled."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,7 +129,13 @@ def main():
     ap.add_argument("--workload", default="llama3-8b-layer",
                     choices=["llama3-8b-layer", "qwen3-8b-sign1-layer", "llama3-8b-long-ctx"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 5 times "
+                         "(the calibration kernel for HBM traffic counters), then exit")
     args = ap.parse_args()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
               "sharding of this path is a design in DESIGN.md, not a measured run",
@@ -159,8 +209,14 @@ def main():
     achieved = gemm_flops[dom] / (dom_us * 1e-6) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None,
                 "avg_us": round(dom_us, 2), "flops_per_launch": gemm_flops[dom]}
+
+    tr = stored_traffic(sh.name, dom)
+    if tr is not None:
+        roofline["traffic"] = tr["bytes"]
+        roofline["traffic_detail"] = tr
 
     cpu = None
     if not args.no_cpu_baseline:
