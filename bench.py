@@ -173,6 +173,16 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # the same K steps without the per-kernel events (launch overhead only)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_plain = e0.elapsed_time(e1) / args.steps
+
     # timed region: K steps bracketed by synchronisation; HIP events from the
     # library's profiler time every kernel on the stream it runs on
     log(f"[bench] timing {args.steps} steps")
@@ -239,6 +249,7 @@ def main():
         "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv
                         for kk, vv in v.items()} for k, v in kernels.items()},
         "wall_s_timed": round(wall, 4),
+        "ms_per_step_without_kernel_events": round(ms_step_plain, 4),
     }
     print(json.dumps(out), flush=True)
 

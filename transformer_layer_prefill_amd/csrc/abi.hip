@@ -71,15 +71,18 @@ tlp_status check_config(const tlp_config* c) {
   return TLP_OK;
 }
 
-// Rows of split-K slices (slices x micro-batch rows) the output and down
-// projections may write for any micro-batch of at most m rows (bf16 path).
-size_t part_rows(const tlp_config& c, int m) {
+// fp32 elements of split-K slices the QKV, output and down projections may
+// write for any micro-batch of at most m rows (bf16 path).
+size_t part_elems(const tlp_config& c, int m) {
   if (c.dtype != TLP_BF16) return 0;
   size_t best = 0;
   for (int r = 1; r <= m; ++r) {
+    const int qkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
     const int a = tlp::gemm_partial_splits(r, c.hidden, c.n_q_heads * c.head_dim);
     const int b = tlp::gemm_partial_splits(r, c.hidden, c.intermediate);
-    const size_t rows = static_cast<size_t>(a > b ? a : b) * r;
+    const size_t ab = static_cast<size_t>(a > b ? a : b) * c.hidden;
+    const size_t q = static_cast<size_t>(tlp::gemm_partial_splits(r, qkv, c.hidden)) * qkv;
+    const size_t rows = (ab > q ? ab : q) * r;
     if (rows > best) best = rows;
   }
   return best;
@@ -100,7 +103,7 @@ Layout layout_of(const tlp_config& c, int m) {
       M * static_cast<size_t>(c.n_q_heads) * c.head_dim * e,  // ATTN
       M * c.intermediate * e,                                 // ACT
       static_cast<size_t>(c.hidden) * 4,                      // HEAD
-      part_rows(c, m) * c.hidden * 4,                          // PART
+      part_elems(c, m) * 4,                                    // PART
   };
   Layout L{};
   size_t o = 0;
@@ -249,12 +252,20 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g.A = xn; g.lda = H;
   g.W = w.w_qkv.data; g.Wscale = w.w_qkv.scales;
   g.M = n; g.N = qkv_dim; g.K = H;
-  g.epi = Epi::Store; g.out = qkv; g.ldo = qkv_dim;
+  int q_parts = 0;
+  const size_t qkv_part_stride = static_cast<size_t>(n) * qkv_dim;
+  if (split) {
+    g.epi = Epi::Partial; g.out = part; g.ldo = qkv_dim; g.out_f32 = true;
+    g.part_stride = qkv_part_stride; g.splits_out = &q_parts;
+  } else {
+    g.epi = Epi::Store; g.out = qkv; g.ldo = qkv_dim;
+  }
   TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemm(g, s));
-  // 3a-3d. QK-norm, RoPE, KV-cache store
-  TLP_LAUNCH(TLP_K_QK_ROPE_KV, launch_qk_rope_store(act, qkv, n, qkv_dim, w.q_norm, w.k_norm, c.qk_norm != 0,
-                                  c.rms_eps, cs, sn, k_layer, v_layer, c.max_seq, start, nq, nkv,
-                                  hd, s));
+  // 3a-3d. (slice sum,) QK-norm, RoPE, KV-cache store
+  TLP_LAUNCH(TLP_K_QK_ROPE_KV,
+             launch_qk_rope_store(act, qkv, n, qkv_dim, part, q_parts, qkv_part_stride, w.q_norm,
+                                  w.k_norm, c.qk_norm != 0, c.rms_eps, cs, sn, k_layer, v_layer,
+                                  c.max_seq, start, nq, nkv, hd, s));
   // 3e. causal GQA attention
   TLP_LAUNCH(TLP_K_ATTENTION, launch_attention(act, qkv, qkv_dim, k_layer, v_layer, attn, qd, n, start, nq, nkv,
                               hd, c.max_seq, s));

@@ -539,7 +539,7 @@ static int big_tiles(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256
 
 int gemm_partial_splits(int M, int N, int K) {
   const int tiles = big_tiles(M, N);
-  int splits = (kCUs + tiles - 1) / tiles;
+  int splits = kCUs / tiles;   // the grid stays within one wave of work items
   if (splits > kMaxSplits) splits = kMaxSplits;
   const int k_tiles = (K + 31) / 32;
   if (splits > k_tiles) splits = k_tiles;

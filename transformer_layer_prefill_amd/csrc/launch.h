@@ -60,9 +60,12 @@ int gemm_partial_splits(int M, int N, int K);
 
 // ---- QK-norm + RoPE + KV-cache store -----------------------------------------
 // Per token t (absolute position start + t): optional per-head RMSNorm of Q and K
-// heads, rotate-half RoPE of Q (in place inside qkv) and K, then K (roped) and V
-// (raw) into cache slot start + t of every kv head of this layer.
-hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const void* q_gain,
+// heads, rotate-half RoPE of Q (written into qkv) and K, then K (roped) and V
+// (raw) into cache slot start + t of every kv head of this layer.  The input row
+// is qkv itself (n_part == 0) or the sum of n_part fp32 split-K slices of
+// row stride qkv_ld, part_stride elements apart.
+hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const float* part,
+                                int n_part, size_t part_stride, const void* q_gain,
                                 const void* k_gain, bool qk_norm, float eps,
                                 const float* rope_cos, const float* rope_sin, void* k_layer,
                                 void* v_layer, int max_seq, int start, int nq, int nkv,

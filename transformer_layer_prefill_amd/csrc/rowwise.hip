@@ -47,7 +47,8 @@ __device__ __forceinline__ void store8(float* p, const float v[8]) {
 // gain is given.  Up to 8 chunks of 8 elements per thread (H <= 16384).
 template <typename T, bool XF32, bool NORM_F32>
 __global__ __launch_bounds__(256) void rownorm_kernel(RowArgs a) {
-  constexpr int CH = 8;
+  constexpr int CH = 8;       // chunks of 8 elements per thread (H <= 16384)
+  constexpr int MAXP = 8;     // partial slices summed per row
   __shared__ float red[4];
   const int r = blockIdx.x;
   const int chunks = a.H >> 3;
@@ -58,16 +59,20 @@ __global__ __launch_bounds__(256) void rownorm_kernel(RowArgs a) {
   for (int c = 0; c < CH; ++c) {
     const int idx = threadIdx.x + c * 256;
     if (idx >= chunks) break;
+    // issue the row chunk and every partial slice before summing
     if constexpr (XF32)
       load8(static_cast<const float*>(a.x) + static_cast<size_t>(r) * a.ldx + idx * 8, v[c]);
     else
       load8(static_cast<const T*>(a.x) + static_cast<size_t>(r) * a.ldx + idx * 8, v[c]);
-    for (int p = 0; p < a.n_part; ++p) {
-      float q[8];
-      load8(a.part + p * a.part_stride + roff + idx * 8, q);
+    float q[MAXP][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[c][i] += q[i];
-    }
+    for (int p = 0; p < MAXP; ++p)
+      if (p < a.n_part) load8(a.part + p * a.part_stride + roff + idx * 8, q[p]);
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (p < a.n_part)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[c][i] += q[p][i];
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss += v[c][i] * v[c][i];
     if (a.res_out) store8(a.res_out + roff + idx * 8, v[c]);
@@ -107,17 +112,21 @@ static hipError_t rownorm_t(const RowArgs& a, hipStream_t s) {
 
 hipError_t launch_rownorm(Act act, const RowArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
-  if (a.H % 8 || a.H > 8 * 8 * 256) return hipErrorInvalidValue;
+  if (a.H % 8 || a.H > 8 * 8 * 256 || a.n_part > 8) return hipErrorInvalidValue;
   return act == Act::F32 ? rownorm_t<float>(a, s) : rownorm_t<uint16_t>(a, s);
 }
 
-// One block per token; wave w walks heads w, w+4, ... of [Q heads | K heads | V heads].
+// Block (t, y) covers token t; its wave w takes head 4y + w of [Q heads | K heads | V heads].
 // Lane i owns the rotate-half pair (i, i + hd/2) of a Q/K head, so the head's
 // RMSNorm is a single wavefront reduction and RoPE needs no data exchange.
+// The projected row is either qkv itself (activation type) or, when the QKV
+// GEMM split K, the sum of its n_part fp32 slices; roped Q is written back into
+// qkv for the attention kernel either way.
 template <typename T>
 __global__ __launch_bounds__(256) void qk_rope_store_kernel(
-    T* __restrict__ qkv, int qkv_ld, const T* __restrict__ q_gain,
-    const T* __restrict__ k_gain, int qk_norm, float eps, const float* __restrict__ rope_cos,
+    T* __restrict__ qkv, int qkv_ld, const float* __restrict__ part, int n_part,
+    size_t part_stride, const T* __restrict__ q_gain, const T* __restrict__ k_gain,
+    int qk_norm, float eps, const float* __restrict__ rope_cos,
     const float* __restrict__ rope_sin, T* __restrict__ k_layer, T* __restrict__ v_layer,
     int max_seq, int start, int nq, int nkv, int hd) {
   const int t = blockIdx.x;
@@ -125,20 +134,31 @@ __global__ __launch_bounds__(256) void qk_rope_store_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = hd >> 1;
   T* row = qkv + static_cast<size_t>(t) * qkv_ld;
+  const float* prow = part + static_cast<size_t>(t) * qkv_ld;
   const int n_heads = nq + 2 * nkv;
-  for (int hh = wave; hh < n_heads; hh += 4) {
-    T* src = row + hh * hd;
+  auto in = [&](int col) -> float {
+    if (n_part == 0) return to_f32(row[col]);
+    constexpr int MAXP = 8;   // issue every slice load before summing
+    float q[MAXP];
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) q[p] = p < n_part ? prow[p * part_stride + col] : 0.f;
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) v += q[p];
+    return v;
+  };
+  for (int hh = blockIdx.y * 4 + wave; hh < n_heads; hh += gridDim.y * 4) {
     if (hh >= nq + nkv) {  // V head: raw copy into the cache slot
       const int j = hh - nq - nkv;
       T* dst = v_layer + (static_cast<size_t>(j) * max_seq + pos) * hd;
-      for (int i = lane; i < hd; i += 64) dst[i] = src[i];
+      for (int i = lane; i < hd; i += 64) dst[i] = from_f32<T>(in(hh * hd + i));
       continue;
     }
     const bool active = lane < half;
     float x1 = 0.f, x2 = 0.f;
     if (active) {
-      x1 = to_f32(src[lane]);
-      x2 = to_f32(src[lane + half]);
+      x1 = in(hh * hd + lane);
+      x2 = in(hh * hd + lane + half);
     }
     if (qk_norm) {
       const float ss = wave_sum(x1 * x1 + x2 * x2);
@@ -154,31 +174,34 @@ __global__ __launch_bounds__(256) void qk_rope_store_kernel(
     const float sn = rope_sin[static_cast<size_t>(pos) * half + lane];
     const float y1 = x1 * c - x2 * sn;
     const float y2 = x2 * c + x1 * sn;
-    T* dst = hh < nq ? src : k_layer + (static_cast<size_t>(hh - nq) * max_seq + pos) * hd;
+    T* dst = hh < nq ? row + hh * hd
+                     : k_layer + (static_cast<size_t>(hh - nq) * max_seq + pos) * hd;
     dst[lane] = from_f32<T>(y1);
     dst[lane + half] = from_f32<T>(y2);
   }
 }
 
-hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const void* q_gain,
+hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const float* part,
+                                int n_part, size_t part_stride, const void* q_gain,
                                 const void* k_gain, bool qk_norm, float eps,
                                 const float* rope_cos, const float* rope_sin, void* k_layer,
                                 void* v_layer, int max_seq, int start, int nq, int nkv,
                                 int head_dim, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  dim3 grid(M), block(256);
+  if (n_part > 8) return hipErrorInvalidValue;
+  dim3 grid(M, (nq + 2 * nkv + 3) / 4), block(256);
   if (act == Act::F32)
     qk_rope_store_kernel<float><<<grid, block, 0, s>>>(
-        static_cast<float*>(qkv), qkv_ld, static_cast<const float*>(q_gain),
-        static_cast<const float*>(k_gain), qk_norm ? 1 : 0, eps, rope_cos, rope_sin,
-        static_cast<float*>(k_layer), static_cast<float*>(v_layer), max_seq, start, nq, nkv,
-        head_dim);
+        static_cast<float*>(qkv), qkv_ld, part, n_part, part_stride,
+        static_cast<const float*>(q_gain), static_cast<const float*>(k_gain), qk_norm ? 1 : 0,
+        eps, rope_cos, rope_sin, static_cast<float*>(k_layer), static_cast<float*>(v_layer),
+        max_seq, start, nq, nkv, head_dim);
   else
     qk_rope_store_kernel<uint16_t><<<grid, block, 0, s>>>(
-        static_cast<uint16_t*>(qkv), qkv_ld, static_cast<const uint16_t*>(q_gain),
-        static_cast<const uint16_t*>(k_gain), qk_norm ? 1 : 0, eps, rope_cos, rope_sin,
-        static_cast<uint16_t*>(k_layer), static_cast<uint16_t*>(v_layer), max_seq, start, nq,
-        nkv, head_dim);
+        static_cast<uint16_t*>(qkv), qkv_ld, part, n_part, part_stride,
+        static_cast<const uint16_t*>(q_gain), static_cast<const uint16_t*>(k_gain),
+        qk_norm ? 1 : 0, eps, rope_cos, rope_sin, static_cast<uint16_t*>(k_layer),
+        static_cast<uint16_t*>(v_layer), max_seq, start, nq, nkv, head_dim);
   return hipGetLastError();
 }
 
