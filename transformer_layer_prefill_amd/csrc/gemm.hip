@@ -278,31 +278,30 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 }
 
 // ---- bf16 kernel with direct global->LDS loads ------------------------------
-// Dense weights with K a multiple of 32.  Tiles are 32 wide in K and staged
-// through a 5-deep LDS ring (160 KB at 256x256) filled by
-// global_load_lds_dwordx4 (no register staging), so up to three tiles are in
-// flight while one is multiplied.  Each DMA
-// instruction writes 1 KB (16 rows of 64 B) contiguously; lane l of it fetches
-// the 16-byte chunk (l%4) ^ swz(row) of row l/4, which stores chunk c of row r
-// at slot c ^ swz(r) and keeps the fragment reads free of bank conflicts.
-// Rows past M or N are clamped to a valid row; their products land in
-// discarded outputs.
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
+// Dense weights with K a multiple of 64.  Tiles are 64 wide in K (one full
+// 128-byte line per row, which streams much faster than half lines) and are
+// copied global -> LDS by global_load_lds_dwordx4 into a double buffer, so
+// there is no register staging.  Each DMA instruction writes 1 KB (8 rows of
+// 128 B) contiguously; lane l of it fetches the 16-byte chunk
+// (l%8) ^ swz(row) of row l/8, which stores chunk c of row r at slot
+// c ^ swz(r): any 8 consecutive rows, and any 16 rows taken as 8 pairs, read
+// at one chunk hit distinct banks.  Rows past M or N are clamped to a valid
+// row; their products land in discarded outputs.
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) {
-  constexpr int BK = 32, S = 5;
+  constexpr int BK = 64;
+  constexpr int ROWB = BK * 2;          // 128 bytes
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;  // DMA blocks per wave
-  constexpr int LOADS = A_PW + B_PW;                                       // per wave per tile
   static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "DMA split");
   static_assert(EPI != 2 || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
-  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int wi = xcd_tile(blockIdx.x, gridDim.x);
   const int split = wi % g.splits, t = wi / g.splits;
@@ -316,18 +315,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
   const uint16_t* W = static_cast<const uint16_t*>(g.W);
 
   // global source rows of this lane's DMA chunks (fixed over the K loop)
-  const int drow = lane >> 2, dslot = lane & 3;
+  const int drow = lane >> 3, dslot = lane & 7;
   const uint16_t* a_src[A_PW];
   const uint16_t* b_src[B_PW];
 #pragma unroll
   for (int j = 0; j < A_PW; ++j) {
-    const int row = (wave * A_PW + j) * 16 + drow;
+    const int row = (wave * A_PW + j) * 8 + drow;
     const int m = min(m0 + row, g.M - 1);
-    a_src[j] = g.A + static_cast<size_t>(m) * g.lda + (dslot ^ swz4(row)) * 8;
+    a_src[j] = g.A + static_cast<size_t>(m) * g.lda + (dslot ^ swz8(row)) * 8;
   }
 #pragma unroll
   for (int j = 0; j < B_PW; ++j) {
-    const int row = (wave * B_PW + j) * 16 + drow;
+    const int row = (wave * B_PW + j) * 8 + drow;
     int n;
     if constexpr (EPI == 2) {
       const int w = row / TN, rr = row % TN;
@@ -336,12 +335,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
     } else {
       n = min(nt * BN + row, g.N - 1);
     }
-    b_src[j] = W + static_cast<size_t>(n) * g.K + (dslot ^ swz4(row)) * 8;
+    b_src[j] = W + static_cast<size_t>(n) * g.K + (dslot ^ swz8(row)) * 8;
   }
 
   auto issue = [&](int kt) __attribute__((always_inline)) {
     const int k0 = k_begin + kt * BK;
-    char* st = smem + (kt % S) * STAGE;
+    char* st = smem + (kt & 1) * STAGE;
 #pragma unroll
     for (int j = 0; j < A_PW; ++j) dma16(a_src[j] + k0, st + (wave * A_PW + j) * 1024);
 #pragma unroll
@@ -356,66 +355,72 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fragment byte offsets inside a stage: row base*64 + swizzled chunk
-  const int sw = swz4(lr);
-  const int a_off = (wm * TM + lr) * 64, b_off = A_BYTES + (wn * TN + lr) * 64;
-  const int c0 = ((0 * 2 + lh) ^ sw) << 4, c1 = ((1 * 2 + lh) ^ sw) << 4;
+  // fragment byte offsets inside a stage: row * 128 + swizzled chunk; the
+  // fragment rows are 32-aligned, so swz(row) = swz(lr)
+  const int sw = swz8(lr);
+  const int a_off = (wm * TM + lr) * ROWB, b_off = A_BYTES + (wn * TN + lr) * ROWB;
+  int ch[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) ch[kk] = ((kk * 2 + lh) ^ sw) << 4;
   bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
 #define TLP_FRAGS(AF, BF, ST, C)                                                             \
   _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                     \
-      *reinterpret_cast<const bf16x8_t*>((ST) + a_off + i * 32 * 64 + (C));                  \
+      *reinterpret_cast<const bf16x8_t*>((ST) + a_off + i * 32 * ROWB + (C));                \
   _Pragma("unroll") for (int j = 0; j < FN; ++j) BF[j] =                                     \
-      *reinterpret_cast<const bf16x8_t*>((ST) + b_off + j * 32 * 64 + (C));
+      *reinterpret_cast<const bf16x8_t*>((ST) + b_off + j * 32 * ROWB + (C));
 #define TLP_MMA(AF, BF)                                                                      \
   _Pragma("unroll") for (int i = 0; i < FM; ++i)                                             \
   _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AF[i], BF[j], acc[i][j], 0, 0, 0);
 
-  // Schedule per 32-wide tile kt (two 16-wide k-steps):
-  //   read step-1 fragments of kt | MFMAs of step 0
-  //   wait for tile kt+1, barrier, refill the stage of tile kt-1,
-  //   read step-0 fragments of kt+1 | MFMAs of step 1
-  // so LDS reads always overlap MFMAs and the barrier sits between MFMA blocks.
+  // Schedule per 64-wide tile kt (four 16-wide k-steps, fragments of step s+1
+  // read during the MFMAs of step s): after the MFMAs of step 2 are issued,
+  // wait for tile kt+1, barrier (every wave has read all of tile kt), refill
+  // tile kt's stage with tile kt+2, read step 0 of tile kt+1, then step 3's MFMAs.
   const int nk = (k_end - k_begin) / BK;
-#pragma unroll
-  for (int p = 0; p < S - 1; ++p)
-    if (p < nk) issue(p);
-  // tile 0 has landed once the tiles issued after it are all that remain
-  if (nk > S - 2) __builtin_amdgcn_s_waitcnt(VmWait<(S - 2) * LOADS>::imm);
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 1) __builtin_amdgcn_s_waitcnt(VmWait<A_PW + B_PW>::imm);
   else __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  TLP_FRAGS(af0, bf0, smem, c0)
+  lds_barrier();
+  TLP_FRAGS(af0, bf0, smem, ch[0])
   // drain every scalar load too: a scalar load still pending at the loop
   // entry would force full LDS waits inside the loop
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
 
-  // Main loop: every iteration has a next tile, so the LDS reads are the same
-  // on every path and the compiler's wait counting stays exact.
   int kt = 0;
   for (; kt + 1 < nk; ++kt) {
-    const char* st = smem + (kt % S) * STAGE;
-    TLP_FRAGS(af1, bf1, st, c1)
+    const char* st = smem + (kt & 1) * STAGE;
+    TLP_FRAGS(af1, bf1, st, ch[1])
     __builtin_amdgcn_sched_barrier(0);
     TLP_MMA(af0, bf0)
     __builtin_amdgcn_sched_barrier(0);
-    // tiles issued so far end at kt+S-2; tile kt+1 has landed once at most the
-    // (up to S-3) tiles after it are still in flight
-    if (kt + S - 2 < nk) __builtin_amdgcn_s_waitcnt(VmWait<(S - 3) * LOADS>::imm);
-    else __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
-    // barrier without the full memory fence of __syncthreads, which would also
-    // wait for the DMA loads of the tiles still in flight
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // every wave has read all of tile kt-1: its stage takes tile kt+S-1
-    if (kt + S - 1 < nk) issue(kt + S - 1);
-    const char* st1 = smem + ((kt + 1) % S) * STAGE;
-    TLP_FRAGS(af0, bf0, st1, c0)
+    TLP_FRAGS(af0, bf0, st, ch[2])
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af1, bf1)
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_FRAGS(af1, bf1, st, ch[3])
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af0, bf0)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // tile kt+1, the only copy in flight
+    lds_barrier();
+    if (kt + 2 < nk) issue(kt + 2);
+    const char* st1 = smem + ((kt + 1) & 1) * STAGE;
+    TLP_FRAGS(af0, bf0, st1, ch[0])
     __builtin_amdgcn_sched_barrier(0);
     TLP_MMA(af1, bf1)
     __builtin_amdgcn_sched_barrier(0);
   }
   {
-    const char* st = smem + (kt % S) * STAGE;
-    TLP_FRAGS(af1, bf1, st, c1)
+    const char* st = smem + (kt & 1) * STAGE;
+    TLP_FRAGS(af1, bf1, st, ch[1])
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af0, bf0)
+    TLP_FRAGS(af0, bf0, st, ch[2])
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af1, bf1)
+    TLP_FRAGS(af1, bf1, st, ch[3])
     __builtin_amdgcn_sched_barrier(0);
     TLP_MMA(af0, bf0)
     TLP_MMA(af1, bf1)
@@ -508,9 +513,9 @@ static hipError_t run_bf16(GemmArgs g, int splits, hipStream_t s) {
   const int cols = EPI == 2 ? BN / 2 : BN;
   g.m_tiles = (g.M + BM - 1) / BM;
   g.n_tiles = (g.N + cols - 1) / cols;
-  // the direct-to-LDS kernel needs whole 32-wide K tiles; it slices K by 32
-  const bool dma = !SIGN1 && g.K % 32 == 0;
-  const int kt_w = dma ? 32 : 64;
+  // the direct-to-LDS kernel needs whole 64-wide K tiles
+  const bool dma = !SIGN1 && g.K % 64 == 0;
+  const int kt_w = 64;
   const int k_tiles = (g.K + kt_w - 1) / kt_w;
   if (splits > k_tiles) splits = k_tiles;
   if (splits < 1) splits = 1;
@@ -541,7 +546,7 @@ int gemm_partial_splits(int M, int N, int K) {
   const int tiles = big_tiles(M, N);
   int splits = kCUs / tiles;   // the grid stays within one wave of work items
   if (splits > kMaxSplits) splits = kMaxSplits;
-  const int k_tiles = (K + 31) / 32;
+  const int k_tiles = (K + 63) / 64;
   if (splits > k_tiles) splits = k_tiles;
   return splits < 1 ? 1 : splits;
 }
