@@ -174,8 +174,9 @@ def test_chunk_matches_oracle_and_is_chunking_invariant():
             for c_in, c_gpu in ((kc, g_kc), (vc, g_vc)):
                 check_cache_slots(sh, 0, sh.n_tokens, sh.start, c_in[l:l + 1], c_gpu[l:l + 1])
         outs[mb] = g
+    # two GPU results, each within 2e-2 of the exact one, differ by at most twice that
     for mb, g in outs.items():
-        assert rel_err(g, outs[sh.micro_batch]) <= 2e-2
+        assert rel_err(g, outs[sh.micro_batch]) <= 2 * 2e-2
 
 
 @pytest.mark.timeout(900)
@@ -223,6 +224,10 @@ def test_stack32_chunked_prefill():
     e_cl = rel_err(results[1024][3], g_logits)
     log(f"[parity] stack32: k0={e_k:.2e} v0={e_v:.2e} logits={e_l:.2e} "
         f"chunk-invariance hidden={e_c:.2e} logits={e_cl:.2e}")
-    for e in (e_k, e_v, e_l, e_c, e_cl):
+    for e in (e_k, e_v, e_l):
         assert e <= 2e-2
+    # (c) compares two GPU runs, each within 2e-2 of the exact stack output:
+    # by the triangle inequality they may differ by up to twice that
+    for e in (e_c, e_cl):
+        assert e <= 2 * 2e-2
     assert np.all(np.isfinite(g))

@@ -54,13 +54,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const int hpb = a.hpb;
   const int tsub = 4 / hpb;            // 32-token slices per block
   const int bt = 32 * tsub;            // tokens per block
-  const int tile = a.tiles - 1 - static_cast<int>(blockIdx.x);  // longest rows first
+  // Work item w = (kv head j, head quad, tile), tile fastest and longest rows
+  // first.  Blocks are dealt round-robin to the eight XCDs, so block b is
+  // given item (b % 8) * (nb / 8) + b / 8: each XCD then works through a
+  // contiguous range of items, i.e. the tiles of one kv head, whose K/V
+  // blocks its L2 serves to all of them.
+  const int nb = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+  const int w = (nb & 7) ? b : (b & 7) * (nb >> 3) + (b >> 3);
+  const int tile = a.tiles - 1 - w % a.tiles;
   const int quads = a.group / hpb;
-  const int j = blockIdx.y / quads, quad = blockIdx.y % quads;
+  const int jq = w / a.tiles;
+  const int j = jq / quads, quad = jq % quads;
   const int h = j * a.group + quad * hpb + wave % hpb;
-  const int t = tile * bt + (wave / hpb) * 32 + lr;   // this lane's query token
+  const int t0w = tile * bt + (wave / hpb) * 32;      // first query token of this wave
+  const int t = t0w + lr;                             // this lane's query token
   const bool q_ok = t < a.M;
-  const int pos = a.start + (q_ok ? t : 0);
+  const int pos = a.start + t;
+  const int pos_lo = a.start + t0w;                   // every key <= pos_lo is visible to the wave
 
   // Q^T fragments (B operand): lane holds Q[t][ks*16 + lh*8 .. +8]
   bf16x8_t qf[KS];
@@ -101,7 +111,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+  // Running maximum in the log2 domain (scores times log2(e)/sqrt(hd)).  It
+  // is only raised when a block's maximum exceeds it by more than 8, so the
+  // weights exp2(s - m_run) stay below 256 and the rescale of o and l is
+  // skipped for most blocks; o / l is the same for any such reference value.
   float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
 
   // V^T transposing reads: lane group g = lane/16 covers head dims
   // (g%2)*16 .. +16 of a 32-wide block for key half lh = g/2; source lane
@@ -132,35 +147,45 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[hb], 0, 0, 0);
       }
     }
+    // the causal mask only cuts blocks that reach past the wave's first query
+    if (key0 + KB - 1 > pos_lo) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + hb * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+          s[hb][r] = key <= pos ? s[hb][r] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + hb * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-        const float v = key <= pos ? s[hb][r] * a.scale_log2 : -INFINITY;
-        s[hb][r] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);     // finite: key 0 is visible to every row
-    const float alpha = fast_exp2(m_run - m_new);
+    const float m_blk = mx * c;   // finite in block 0: key 0 is visible to every row
+    if (__ballot(m_blk > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, m_blk);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    }
+    const float neg_m = -m_run;
     float psum = 0.f;
     bf16x8_t pf[4];   // B operand of step 2*hb + half: slots (lh, e) <- r = 8*half + e
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[hb][r] - m_new);
+        const float p = fast_exp2(fmaf(s[hb][r], c, neg_m));
         psum += p;
         pf[hb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p);
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < DB; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    l_run += psum;
 
     // O^T += V^T P^T.  Slot (lh, e) of step (hb, half) is key
     // hb*32 + half*16 + 8*(e/4) + 4*lh + e%4, matching the score layout above;
@@ -280,7 +305,7 @@ hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_laye
   const int bt = 32 * (4 / a.hpb);
   a.tiles = (M + bt - 1) / bt;
   a.scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
-  dim3 grid(a.tiles, nkv * (a.group / a.hpb));
+  dim3 grid(a.tiles * nkv * (a.group / a.hpb));
   if (head_dim == 128)
     attn_fwd_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
   else
