@@ -83,6 +83,11 @@ SMALL = [
     _small("bf16-start0-long-rows", n_tokens=300, start=0, max_seq=300),
     _small("f32-g4-ragged", hidden=256, inter=344, n_tokens=70, start=9, max_seq=96,
            dtype="f32", qk_norm=True),
+    # enough (kv head, 256-token) tiles to fill the GPU: eight-wavefront attention blocks
+    _small("bf16-8wave-g1-hd64", hidden=256, inter=512, nq=32, nkv=32, head_dim=64,
+           n_tokens=2000, start=37, max_seq=2048),
+    _small("bf16-8wave-g4-ragged", hidden=256, inter=512, nq=32, nkv=8, head_dim=128,
+           n_tokens=1990, start=0, max_seq=2048),
 ]
 
 

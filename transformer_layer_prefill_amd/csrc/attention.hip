@@ -6,9 +6,9 @@
 // flash-style kernel with an online softmax and no score buffer.
 //
 // bf16 kernel (gfx950 MFMA).  A block owns one kv head and a tile of query
-// tokens; its four wavefronts are (query head of the group, 32-token slice)
-// pairs that share every K/V block staged in LDS, so K/V are read once per
-// group.  Per 64-key block a wavefront computes S^T = K Q^T with
+// tokens; its four or eight wavefronts are (query head of the group, 32-token
+// slice) pairs that share every K/V block staged in LDS, so K/V are read once
+// per group and tile.  Per 64-key block a wavefront computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (lane = query, 32 key scores per lane), runs the
 // online softmax in fp32 with exp2, and accumulates O^T = V^T P^T, taking P
 // straight from the score registers and V^T from transposing LDS reads.
@@ -26,33 +26,46 @@ struct AttnArgs {
   int M, start, nq, nkv, max_seq;
   int group;      // nq / nkv
   int hpb;        // query heads per block (min(group, 4))
+  int waves;      // wavefronts per block (4 or 8): waves / hpb 32-token slices
   int tiles;      // token tiles
   float scale_log2;  // log2(e) / sqrt(hd)
 };
 
-// K and V blocks of 64 keys are copied global -> LDS with DMA into a double
-// buffer (the next block streams in while the current one is multiplied).
-// Rows are stored as 16-byte chunks, chunk c of key row r at slot c ^ swz(r):
-// K uses r % 8 so the eight rows of a b128 fragment read hit distinct banks,
-// V uses 2 * (r % 4) so the four rows of a transposing read do.  Key rows past
+// K and V blocks of 64 keys are copied global -> LDS with DMA into rings of
+// three K and two V slots: while block kb's softmax runs on the VALUs, the
+// MFMAs already compute block kb+1's scores, and the copies of K(kb+2) and
+// V(kb+1) are in flight.
+// Rows are stored as 16-byte chunks, chunk c of key row r at slot c ^ swz(r).
+// The LDS has 64 banks (256 bytes per cycle): a b128 read is served 16 lanes
+// at a time, a transposing b64 read 32 lanes at a time.  With RPL = 256 /
+// row bytes key rows per bank line, K uses (r / RPL) % chunks so the 16 rows
+// of a b128 step cover all banks once, and V uses 4 * ((r / RPL) % (chunks /
+// 4)) so the four rows x 64 bytes of a transposing step do.  Key rows past
 // the last visible key are clamped to it (finite data that the mask gives a
 // zero weight), so unwritten cache slots never reach the products.
-template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int KB = 64;                 // keys per block
   constexpr int ROWB = HD * 2;           // bytes per key row
   constexpr int CH = ROWB / 16;          // 16-byte chunks per row
   constexpr int RPI = 1024 / ROWB;       // rows per DMA instruction
   constexpr int TILE = KB * ROWB;        // bytes of one K (or V) block
-  constexpr int PW = TILE / 1024 / 4;    // DMA instructions per wave per K (or V) block
+  constexpr int PW = TILE / 1024 / NW;   // DMA instructions per wave per K (or V) block
   constexpr int KS = HD / 16;            // k-steps of the QK^T contraction
   constexpr int DB = HD / 32;            // 32-wide blocks of the head dimension
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];   // [buffer][K | V]
+  constexpr int RPL = 256 / ROWB;        // key rows per LDS bank line
+  auto swz_k = [](int r) { return (r / RPL) & (CH - 1); };
+  auto swz_v = [](int r) { return ((r / RPL) & (CH / 4 - 1)) * 4; };
+  constexpr int SK = 3, SV = 2;          // ring slots for K and V blocks
+  __shared__ __attribute__((aligned(1024))) char smem[(SK + SV) * TILE];
+  char* const kring = smem;
+  char* const vring = smem + SK * TILE;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
   const int lr = lane & 31, lh = lane >> 5;
   const int hpb = a.hpb;
-  const int tsub = 4 / hpb;            // 32-token slices per block
+  const int tsub = NW / hpb;           // 32-token slices per block
   const int bt = 32 * tsub;            // tokens per block
   // Work item w = (kv head j, head quad, tile), tile fastest and longest rows
   // first.  Blocks are dealt round-robin to the eight XCDs, so block b is
@@ -91,18 +104,55 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const uint16_t* kbase = a.k + static_cast<size_t>(j) * a.max_seq * HD;
   const uint16_t* vbase = a.v + static_cast<size_t>(j) * a.max_seq * HD;
 
-  // DMA: instruction q covers key rows q*RPI .. +RPI; lane -> (row, slot)
+  // DMA: instruction q covers key rows q*RPI .. +RPI; lane -> (row, slot).
+  // Row `row` of block kb is key kb*KB + row; only a block that reaches past
+  // kv_end needs its keys clamped.
   const int d_row = lane / CH, d_slot = lane % CH;
-  auto issue = [&](int kb) __attribute__((always_inline)) {
-    char* st = smem + (kb & 1) * 2 * TILE;
+  // byte offsets of this lane's DMA chunks inside a block (the block base is
+  // uniform, so each copy is a scalar base plus a 32-bit vector offset)
+  uint32_t k_off[PW], v_off[PW];
 #pragma unroll
-    for (int jj = 0; jj < PW; ++jj) {
-      const int q = wave * PW + jj;
-      const int row = q * RPI + d_row;
-      const int key = min(kb * KB + row, kv_end - 1);
-      dma16(kbase + static_cast<size_t>(key) * HD + (d_slot ^ (row & 7)) * 8, st + q * 1024);
-      dma16(vbase + static_cast<size_t>(key) * HD + (d_slot ^ ((row & 3) * 2)) * 8,
-            st + TILE + q * 1024);
+  for (int jj = 0; jj < PW; ++jj) {
+    const int row = (wave * PW + jj) * RPI + d_row;
+    k_off[jj] = row * ROWB + (d_slot ^ swz_k(row)) * 16;
+    v_off[jj] = row * ROWB + (d_slot ^ swz_v(row)) * 16;
+  }
+  const int full_blocks = kv_end / KB;
+  auto issue = [&](int kb, bool is_v) __attribute__((always_inline)) {
+    char* st = is_v ? vring + (kb % SV) * TILE : kring + (kb % SK) * TILE;
+    const uint16_t* base = is_v ? vbase : kbase;
+    if (kb < full_blocks) {
+      const char* blk = reinterpret_cast<const char*>(base) + static_cast<size_t>(kb) * TILE;
+#pragma unroll
+      for (int jj = 0; jj < PW; ++jj)
+        dma16(blk + (is_v ? v_off[jj] : k_off[jj]), st + (wave * PW + jj) * 1024);
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < PW; ++jj) {
+        const int q = wave * PW + jj;
+        const int row = q * RPI + d_row;
+        const int key = min(kb * KB + row, kv_end - 1);
+        const int sw = is_v ? swz_v(row) : swz_k(row);
+        dma16(base + static_cast<size_t>(key) * HD + (d_slot ^ sw) * 8, st + q * 1024);
+      }
+    }
+  };
+
+  // S^T of block kb for two 32-key halves: lane (query lr) gets keys
+  // 8*(r/4) + 4*lh + r%4 of each half
+  auto scores = [&](int kb, f32x16_t (&sc)[2]) __attribute__((always_inline)) {
+    const char* Kt = kring + (kb % SK) * TILE;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[hb][r] = 0.f;
+      const int krow = hb * 32 + lr;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+            Kt + krow * ROWB + (((ks * 2 + lh) ^ swz_k(krow)) << 4));
+        sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[hb], 0, 0, 0);
+      }
     }
   };
 
@@ -124,29 +174,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const int tr_key = (lane & 15) >> 2;                       // + key base
   const int tr_dim = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;  // + 32*db
 
-  issue(0);
-  for (int kb = 0; kb < nkb; ++kb) {
+  // prologue: K(0), V(0), K(1) in flight; scores of block 0 once K(0) landed
+  issue(0, false);
+  issue(0, true);
+  if (nkb > 1) {
+    issue(1, false);
+    __builtin_amdgcn_s_waitcnt(VmWait<2 * PW>::imm);
+  } else {
+    __builtin_amdgcn_s_waitcnt(VmWait<PW>::imm);
+  }
+  lds_barrier();
+  // One key block: softmax of block kb from its scores s, with the scores of
+  // block kb+1 computed into s_next on the way.  The loop alternates the two
+  // score arrays so that no registers are copied between blocks.
+  auto step = [&](int kb, f32x16_t (&s)[2], f32x16_t (&s_next)[2]) __attribute__((always_inline)) {
     const int key0 = kb * KB;
-    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wave's copies of block kb
-    lds_barrier();                                 // everyone's; buffer kb+1 is free
-    if (kb + 1 < nkb) issue(kb + 1);
-    const char* Kt = smem + (kb & 1) * 2 * TILE;
-    const char* Vt = Kt + TILE;
-
-    // S^T for two 32-key halves: lane (query lr) gets keys 8*(r/4) + 4*lh + r%4
-    f32x16_t s[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[hb][r] = 0.f;
-      const int krow = hb * 32 + lr;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-            Kt + krow * ROWB + (((ks * 2 + lh) ^ (krow & 7)) << 4));
-        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[hb], 0, 0, 0);
-      }
-    }
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wave's copies of V(kb), K(kb+1)
+    lds_barrier();   // everyone's; V slot of kb-1 and K slot of kb-1 are free
+    if (kb + 1 < nkb) issue(kb + 1, true);
+    if (kb + 2 < nkb) issue(kb + 2, false);
     // the causal mask only cuts blocks that reach past the wave's first query
     if (key0 + KB - 1 > pos_lo) {
 #pragma unroll
@@ -174,22 +220,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
     }
+    // The next block's scores go to the MFMAs while this block's weights are
+    // computed on the VALUs; the schedule below interleaves the two streams
+    // (a wavefront issues in order).  The last iteration recomputes its own
+    // block, whose K slot is still intact.
+    scores(min(kb + 1, nkb - 1), s_next);
     const float neg_m = -m_run;
-    float psum = 0.f;
     bf16x8_t pf[4];   // B operand of step 2*hb + half: slots (lh, e) <- r = 8*half + e
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[hb][r], c, neg_m));
-        psum += p;
-        pf[hb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p);
-      }
-    l_run += psum;
+      for (int r = 0; r < 16; ++r)
+        pf[hb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(fast_exp2(fmaf(s[hb][r], c, neg_m)));
+    // the row sum takes the same bf16 weights the products use, two per dot2
+    float psum0 = 0.f, psum1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = __builtin_bit_cast(uint4, pf[i]);
+      psum0 = dot2_bf16_sum(u.x, psum0);
+      psum1 = dot2_bf16_sum(u.y, psum1);
+      psum0 = dot2_bf16_sum(u.z, psum0);
+      psum1 = dot2_bf16_sum(u.w, psum1);
+    }
+    l_run += psum0 + psum1;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // 4 K fragment reads ahead
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      if (i + 4 < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one score MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU instructions
+    }
 
     // O^T += V^T P^T.  Slot (lh, e) of step (hb, half) is key
     // hb*32 + half*16 + 8*(e/4) + 4*lh + e%4, matching the score layout above;
     // each run of four consecutive keys is one transposing read.
+    const char* Vt = vring + (kb % SV) * TILE;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
       const int dim = d * 32 + tr_dim;
@@ -197,15 +262,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       for (int st = 0; st < 4; ++st) {
         const int kbase_r = (st >> 1) * 32 + (st & 1) * 16 + lh * 4 + tr_key;
         const int r0 = kbase_r, r1 = kbase_r + 8;
-        const uint2 lo = lds_read_tr16(Vt + r0 * ROWB + ((((dim >> 3)) ^ ((r0 & 3) * 2)) << 4) +
+        const uint2 lo = lds_read_tr16(Vt + r0 * ROWB + (((dim >> 3) ^ swz_v(r0)) << 4) +
                                        (dim & 7) * 2);
-        const uint2 hi = lds_read_tr16(Vt + r1 * ROWB + ((((dim >> 3)) ^ ((r1 & 3) * 2)) << 4) +
+        const uint2 hi = lds_read_tr16(Vt + r1 * ROWB + (((dim >> 3) ^ swz_v(r1)) << 4) +
                                        (dim & 7) * 2);
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], o[d], 0, 0, 0);
       }
     }
+  };
+
+  f32x16_t sa[2], sb[2];
+  scores(0, sa);
+  int kb = 0;
+  for (; kb + 1 < nkb; kb += 2) {
+    step(kb, sa, sb);
+    step(kb + 1, sb, sa);
   }
+  if (kb < nkb) step(kb, sa, sb);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!q_ok) return;
@@ -302,14 +376,23 @@ hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_laye
   a.max_seq = max_seq;
   a.group = nq / nkv;
   a.hpb = a.group < 4 ? a.group : 4;
-  const int bt = 32 * (4 / a.hpb);
+  // Eight wavefronts per block (one block per CU, K/V copied into LDS once per
+  // CU) when that still gives every CU a block; four (two blocks per CU)
+  // otherwise.
+  const int quads = a.group / a.hpb;
+  const int tiles8 = (M + 32 * (8 / a.hpb) - 1) / (32 * (8 / a.hpb));
+  a.waves = tiles8 * nkv * quads >= 256 ? 8 : 4;
+  const int bt = 32 * (a.waves / a.hpb);
   a.tiles = (M + bt - 1) / bt;
   a.scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
-  dim3 grid(a.tiles * nkv * (a.group / a.hpb));
-  if (head_dim == 128)
-    attn_fwd_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
-  else
-    attn_fwd_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
+  dim3 grid(a.tiles * nkv * quads);
+  if (head_dim == 128) {
+    if (a.waves == 8) attn_fwd_bf16_kernel<128, 8><<<grid, 512, 0, s>>>(a);
+    else attn_fwd_bf16_kernel<128, 4><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (a.waves == 8) attn_fwd_bf16_kernel<64, 8><<<grid, 512, 0, s>>>(a);
+    else attn_fwd_bf16_kernel<64, 4><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -68,6 +68,13 @@ __device__ __forceinline__ float block_sum(float v, float* red /* LDS, NW floats
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + lo + hi for a pair of bf16 values packed in one word (v_dot2 with 1.0)
+__device__ __forceinline__ float dot2_bf16_sum(uint32_t pair, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair),
+                                         __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
+}
+
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 // 16-byte global -> LDS copy per lane (global_load_lds_dwordx4); `lds` must be
