@@ -48,6 +48,23 @@ def layer_flops(sh, n, start):
     return gemm, 4 * hd * nq * keys
 
 
+def kernel_bytes(sh, n, start):
+    """Algorithmic HBM bytes per launch: weights read once, activation rows in
+    and out (bf16), and the K/V slots attention reads."""
+    H, I, hd, nq, nkv = sh.hidden, sh.inter, sh.head_dim, sh.nq, sh.nkv
+    qkv = (nq + 2 * nkv) * hd
+
+    def gemm(n_out, k):
+        return 2 * (n_out * k + n * k + n * n_out)
+    return {
+        "qkv_gemm": gemm(qkv, H),
+        "o_gemm": gemm(H, nq * hd),
+        "gate_up_gemm": 2 * (2 * I * H + n * H + n * I),
+        "down_gemm": gemm(H, I),
+        "attention": 2 * 2 * (start + n) * nkv * hd + 2 * 2 * n * nq * hd,
+    }
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -128,7 +145,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3-8b-layer",
-                    choices=["llama3-8b-layer", "qwen3-8b-sign1-layer", "llama3-8b-long-ctx"])
+                    choices=["llama3-8b-layer", "qwen3-8b-sign1-layer", "llama3-8b-long-ctx",
+                             "llama3-8b-decode", "llama3-8b-long-decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times "
@@ -174,20 +192,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # the same K steps without the per-kernel events (launch overhead only)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step_plain = e0.elapsed_time(e1) / args.steps
-
-    # timed region: K steps bracketed by synchronisation; HIP events from the
-    # library's profiler time every kernel on the stream it runs on
+    # timed region: K steps bracketed by synchronisation, nothing else on the
+    # stream; `value` comes from here
     log(f"[bench] timing {args.steps} steps")
-    tlp.profile_begin()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -197,10 +204,22 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    prof = tlp.profile_end()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    ms_step = ev0.elapsed_time(ev1) / args.steps
     value = sh.n_tokens / (ms_step * 1e-3)
+
+    # the same K steps again with the library's profiler on: HIP events on the
+    # kernels' own stream around every launch give the per-kernel times (the
+    # extra event packets lengthen the step a little: ms_per_step_profiled)
+    tlp.profile_begin()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prof = tlp.profile_end()
+    ms_step_prof = e0.elapsed_time(e1) / args.steps
 
     gemm_flops, attn_flops = layer_flops(sh, sh.n_tokens, sh.start)
     kernels = {}
@@ -215,17 +234,30 @@ def main():
         kernels[k]["tflops"] = f / (kernels[k]["avg_us"] * 1e-6) / 1e12
     kernels["attention"]["tflops"] = attn_tflops
 
-    # the dominant kernel: the MFMA-bound kernel with the longest launches
-    # (the gate/up GEMM at short context, attention at long context)
+    # the dominant kernel: the one with the longest launches among the
+    # projections and attention (the gate/up GEMM at short context, attention
+    # at long context).  Prefill micro-batches are MFMA-bound; decode steps
+    # (a few rows) read every weight once per step and are HBM-bound.
     dom_flops = dict(gemm_flops, attention=attn_flops)
     dom = max(dom_flops, key=lambda k: kernels[k]["avg_us"])
     dom_us = kernels[dom]["avg_us"]
-    achieved = dom_flops[dom] / (dom_us * 1e-6) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None,
-                "avg_us": round(dom_us, 2), "flops_per_launch": dom_flops[dom]}
+    if sh.n_tokens > 32:
+        achieved = dom_flops[dom] / (dom_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None,
+                    "avg_us": round(dom_us, 2), "flops_per_launch": dom_flops[dom]}
+    else:
+        nbytes = kernel_bytes(sh, sh.n_tokens, sh.start)[dom]
+        achieved = nbytes / (dom_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": None,
+                    "avg_us": round(dom_us, 2), "bytes_per_launch": nbytes}
+        for k, b in kernel_bytes(sh, sh.n_tokens, sh.start).items():
+            kernels[k]["GBps"] = b / (kernels[k]["avg_us"] * 1e-6) / 1e9
 
     tr = stored_traffic(sh.name, dom)
     if tr is not None:
@@ -253,7 +285,7 @@ def main():
         "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv
                         for kk, vv in v.items()} for k, v in kernels.items()},
         "wall_s_timed": round(wall, 4),
-        "ms_per_step_without_kernel_events": round(ms_step_plain, 4),
+        "ms_per_step_profiled": round(ms_step_prof, 4),
     }
     print(json.dumps(out), flush=True)
 

@@ -172,7 +172,8 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
 /* Kernels as timed by the profiler below. */
 enum { TLP_K_ATTN_NORM = 0, TLP_K_QKV_GEMM = 1, TLP_K_QK_ROPE_KV = 2, TLP_K_ATTENTION = 3,
        TLP_K_O_GEMM = 4, TLP_K_FFN_NORM = 5, TLP_K_GATE_UP_GEMM = 6, TLP_K_DOWN_GEMM = 7,
-       TLP_K_FINAL_NORM = 8, TLP_K_LM_HEAD = 9, TLP_K_OUT_ROWS = 10, TLP_K_COUNT = 11 };
+       TLP_K_FINAL_NORM = 8, TLP_K_LM_HEAD = 9, TLP_K_OUT_ROWS = 10, TLP_K_SWIGLU = 11,
+       TLP_K_ARGMAX = 12, TLP_K_COUNT = 13 };
 
 /* Per-kernel GPU timing, the analog of the per-layer / per-command-buffer
  * profiling switches of the pages (metal_full_layer.rs OXIBONSAI_PROFILE and

@@ -95,6 +95,14 @@ WORKLOADS = {
     "llama3-8b-long-ctx": Shape("llama3-8b-long-ctx", hidden=4096, inter=14336, nq=32,
                                 nkv=8, head_dim=128, qk_norm=False, eps=1e-5, theta=5e5,
                                 n_tokens=2048, start=30720, max_seq=32768, seed=1005),
+    # token-by-token decode steps of the same layer: one token after a full
+    # 4096-slot context, and after a 32767-slot context
+    "llama3-8b-decode": Shape("llama3-8b-decode", hidden=4096, inter=14336, nq=32, nkv=8,
+                              head_dim=128, qk_norm=False, eps=1e-5, theta=5e5,
+                              n_tokens=1, start=4095, max_seq=4096, seed=1002),
+    "llama3-8b-long-decode": Shape("llama3-8b-long-decode", hidden=4096, inter=14336, nq=32,
+                                   nkv=8, head_dim=128, qk_norm=False, eps=1e-5, theta=5e5,
+                                   n_tokens=1, start=32767, max_seq=32768, seed=1005),
 }
 
 

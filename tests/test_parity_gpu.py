@@ -106,6 +106,39 @@ def test_sign1_small_layer():
                         start=16, max_seq=128, qk_norm=True, eps=1e-6, wformat="sign1"))
 
 
+# Decode steps and short batches (<= 32 rows): skinny projections, and split-KV
+# attention when few (tile, head) blocks face a long cache.
+DECODE = [
+    _small("decode-g2-split", hidden=256, inter=512, nq=4, nkv=2, n_tokens=3, start=900,
+           max_seq=1024),
+    _small("decode-g1-hd64-qknorm", hidden=384, inter=1024, nq=4, nkv=4, head_dim=64,
+           qk_norm=True, eps=1e-6, n_tokens=1, start=2000, max_seq=2048),
+    _small("decode-g4-32rows-raggedK", n_tokens=32, start=1500, max_seq=1600),
+    _small("decode-g8-hd64-ragged", hidden=512, inter=776, nq=16, nkv=2, head_dim=64,
+           n_tokens=9, start=700, max_seq=720),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE, ids=[s.name for s in DECODE])
+def test_decode_layer(shape):
+    _check_layer(shape)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("n,start", [(1, 4095), (16, 2000)])
+def test_decode_llama3(n, start):
+    sh = synth.WORKLOADS["llama3-8b-layer"].replace(name=f"llama3-8b-decode-{n}@{start}",
+                                                     n_tokens=n, start=start)
+    _check_layer(sh)
+
+
+@pytest.mark.timeout(600)
+def test_decode_long_ctx():
+    sh = synth.WORKLOADS["llama3-8b-long-ctx"].replace(name="llama3-8b-decode-1@32767",
+                                                        n_tokens=1, start=32767)
+    _check_layer(sh)
+
+
 def _sample_rows(n, k=12, seed=0):
     rng = np.random.default_rng(seed)
     rows = set(rng.choice(n, size=min(k, n), replace=False).tolist()) | {0, n - 1}

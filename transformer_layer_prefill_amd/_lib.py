@@ -23,7 +23,8 @@ EXPORTS = ("tlp_workspace_bytes", "tlp_workspace_layout", "tlp_rope_table",
            "tlp_prefill_layer", "tlp_prefill_chunk", "tlp_profile_begin", "tlp_profile_end",
            "tlp_status_string", "tlp_last_error")
 KERNELS = ("attn_norm", "qkv_gemm", "qk_rope_kv", "attention", "o_gemm", "ffn_norm",
-           "gate_up_gemm", "down_gemm", "final_norm", "lm_head", "out_rows")
+           "gate_up_gemm", "down_gemm", "final_norm", "lm_head", "out_rows", "swiglu",
+           "argmax")
 
 
 class TlpError(RuntimeError):

@@ -71,19 +71,36 @@ tlp_status check_config(const tlp_config* c) {
   return TLP_OK;
 }
 
-// fp32 elements of split-K slices the QKV, output and down projections may
-// write for any micro-batch of at most m rows (bf16 path).
+// Whether a micro-batch of n rows takes the skinny projections (decode steps
+// and short batches with dense bf16 weights).
+bool skinny_path(const tlp_config& c, int n) {
+  return c.dtype == TLP_BF16 && c.wformat == TLP_W_DENSE && n <= tlp::kSkinnyMaxM;
+}
+
+// fp32 elements of the PART region for any micro-batch of at most m rows
+// (bf16 path): split-K slices of the QKV, output and down projections (and of
+// gate/up on the skinny path), or the split-KV partial results of attention
+// (the two are never live at once).
 size_t part_elems(const tlp_config& c, int m) {
   if (c.dtype != TLP_BF16) return 0;
+  using namespace tlp;
+  const int H = c.hidden, I = c.intermediate, qd = c.n_q_heads * c.head_dim;
+  const int qkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   size_t best = 0;
+  auto take = [&](size_t v) { if (v > best) best = v; };
   for (int r = 1; r <= m; ++r) {
-    const int qkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
-    const int a = tlp::gemm_partial_splits(r, c.hidden, c.n_q_heads * c.head_dim);
-    const int b = tlp::gemm_partial_splits(r, c.hidden, c.intermediate);
-    const size_t ab = static_cast<size_t>(a > b ? a : b) * c.hidden;
-    const size_t q = static_cast<size_t>(tlp::gemm_partial_splits(r, qkv, c.hidden)) * qkv;
-    const size_t rows = (ab > q ? ab : q) * r;
-    if (rows > best) best = rows;
+    if (skinny_path(c, r)) {
+      take(static_cast<size_t>(skinny_splits(qkv, H)) * qkv * r);
+      take(static_cast<size_t>(skinny_splits(H, qd)) * H * r);
+      take(static_cast<size_t>(skinny_splits(2 * I, H)) * 2 * I * r);
+      take(static_cast<size_t>(skinny_splits(H, I)) * H * r);
+    } else {
+      const int a = gemm_partial_splits(r, H, qd);
+      const int b = gemm_partial_splits(r, H, I);
+      take(static_cast<size_t>(a > b ? a : b) * H * r);
+      take(static_cast<size_t>(gemm_partial_splits(r, qkv, H)) * qkv * r);
+    }
+    take(attention_split_floats(r, c.max_seq, c.n_q_heads, c.n_kv_heads, c.head_dim));
   }
   return best;
 }
@@ -91,6 +108,7 @@ size_t part_elems(const tlp_config& c, int m) {
 struct Layout {
   size_t off[TLP_WS_COUNT];
   size_t total;
+  size_t part_floats;   // capacity of the PART region
 };
 
 Layout layout_of(const tlp_config& c, int m) {
@@ -106,6 +124,7 @@ Layout layout_of(const tlp_config& c, int m) {
       part_elems(c, m) * 4,                                    // PART
   };
   Layout L{};
+  L.part_floats = sizes[TLP_WS_PART] / 4;
   size_t o = 0;
   for (int i = 0; i < TLP_WS_COUNT; ++i) {
     L.off[i] = o;
@@ -237,6 +256,7 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   void* k_layer = kc + layer_off;
   void* v_layer = vc + layer_off;
   const bool split = act == Act::BF16;
+  const bool skinny = skinny_path(c, n);
 
   // 1. residual assembly + attention RMSNorm
   RowArgs r{};
@@ -254,21 +274,29 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g.M = n; g.N = qkv_dim; g.K = H;
   int q_parts = 0;
   const size_t qkv_part_stride = static_cast<size_t>(n) * qkv_dim;
-  if (split) {
-    g.epi = Epi::Partial; g.out = part; g.ldo = qkv_dim; g.out_f32 = true;
-    g.part_stride = qkv_part_stride; g.splits_out = &q_parts;
+  if (skinny) {
+    q_parts = skinny_splits(qkv_dim, H);
+    TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemm_skinny(xn, H, w.w_qkv.data, n, qkv_dim, H, part,
+                                                  qkv_dim, qkv_part_stride, q_parts, s));
   } else {
-    g.epi = Epi::Store; g.out = qkv; g.ldo = qkv_dim;
+    if (split) {
+      g.epi = Epi::Partial; g.out = part; g.ldo = qkv_dim; g.out_f32 = true;
+      g.part_stride = qkv_part_stride; g.splits_out = &q_parts;
+    } else {
+      g.epi = Epi::Store; g.out = qkv; g.ldo = qkv_dim;
+    }
+    TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemm(g, s));
   }
-  TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemm(g, s));
   // 3a-3d. (slice sum,) QK-norm, RoPE, KV-cache store
   TLP_LAUNCH(TLP_K_QK_ROPE_KV,
              launch_qk_rope_store(act, qkv, n, qkv_dim, part, q_parts, qkv_part_stride, w.q_norm,
                                   w.k_norm, c.qk_norm != 0, c.rms_eps, cs, sn, k_layer, v_layer,
                                   c.max_seq, start, nq, nkv, hd, s));
   // 3e. causal GQA attention
-  TLP_LAUNCH(TLP_K_ATTENTION, launch_attention(act, qkv, qkv_dim, k_layer, v_layer, attn, qd, n, start, nq, nkv,
-                              hd, c.max_seq, s));
+  // (the PART region is free here: the QKV slices have been summed)
+  TLP_LAUNCH(TLP_K_ATTENTION,
+             launch_attention(act, qkv, qkv_dim, k_layer, v_layer, attn, qd, n, start, nq, nkv,
+                              hd, c.max_seq, split ? part : nullptr, L.part_floats, s));
   // 4. output projection: split-K slices (bf16) or a fused residual add (fp32)
   int o_parts = 0;
   g = GemmCall{};
@@ -276,13 +304,19 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g.A = attn; g.lda = qd;
   g.W = w.w_o.data; g.Wscale = w.w_o.scales;
   g.M = n; g.N = H; g.K = qd;
-  if (split) {
-    g.epi = Epi::Partial; g.out = part; g.ldo = H; g.out_f32 = true;
-    g.part_stride = part_stride; g.splits_out = &o_parts;
+  if (skinny) {
+    o_parts = skinny_splits(H, qd);
+    TLP_LAUNCH(TLP_K_O_GEMM, launch_gemm_skinny(attn, qd, w.w_o.data, n, H, qd, part, H,
+                                                part_stride, o_parts, s));
   } else {
-    g.epi = Epi::Resid; g.out = res; g.ldo = H; g.out_f32 = true; g.resid = res; g.ldr = H;
+    if (split) {
+      g.epi = Epi::Partial; g.out = part; g.ldo = H; g.out_f32 = true;
+      g.part_stride = part_stride; g.splits_out = &o_parts;
+    } else {
+      g.epi = Epi::Resid; g.out = res; g.ldo = H; g.out_f32 = true; g.resid = res; g.ldr = H;
+    }
+    TLP_LAUNCH(TLP_K_O_GEMM, launch_gemm(g, s));
   }
-  TLP_LAUNCH(TLP_K_O_GEMM, launch_gemm(g, s));
   // 5. residual assembly + FFN RMSNorm
   r = RowArgs{};
   r.x = res; r.x_f32 = 1; r.ldx = H;
@@ -297,8 +331,17 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g.A = xn; g.lda = H;
   g.W = w.w_gate_up.data; g.Wscale = w.w_gate_up.scales;
   g.M = n; g.N = I; g.K = H;
-  g.epi = Epi::SwiGLU; g.out = a; g.ldo = I;
-  TLP_LAUNCH(TLP_K_GATE_UP_GEMM, launch_gemm(g, s));
+  if (skinny) {
+    // fp32 slices of [gate ; up] x_n2, then silu(gate) * up
+    const int gu_parts = skinny_splits(2 * I, H);
+    const size_t gu_stride = static_cast<size_t>(n) * 2 * I;
+    TLP_LAUNCH(TLP_K_GATE_UP_GEMM, launch_gemm_skinny(xn, H, w.w_gate_up.data, n, 2 * I, H, part,
+                                                      2 * I, gu_stride, gu_parts, s));
+    TLP_LAUNCH(TLP_K_SWIGLU, launch_swiglu_finish(part, gu_parts, gu_stride, n, I, a, s));
+  } else {
+    g.epi = Epi::SwiGLU; g.out = a; g.ldo = I;
+    TLP_LAUNCH(TLP_K_GATE_UP_GEMM, launch_gemm(g, s));
+  }
   // 7. down projection
   int d_parts = 0;
   g = GemmCall{};
@@ -306,7 +349,9 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g.A = a; g.lda = I;
   g.W = w.w_down.data; g.Wscale = w.w_down.scales;
   g.M = n; g.N = H; g.K = I;
-  if (split) {
+  if (skinny) {
+    d_parts = skinny_splits(H, I);
+  } else if (split) {
     g.epi = Epi::Partial; g.out = part; g.ldo = H; g.out_f32 = true;
     g.part_stride = part_stride; g.splits_out = &d_parts;
   } else {
@@ -314,7 +359,11 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
     g.out = out_act ? out_act : res;
     if (out_act) g.res_out = res;   // the output also stays in the fp32 stream
   }
-  TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm(g, s));
+  if (skinny)
+    TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm_skinny(a, I, w.w_down.data, n, H, I, part, H,
+                                                   part_stride, d_parts, s));
+  else
+    TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm(g, s));
   *out_parts = 0;
   if (split) {
     if (out_act) {

@@ -29,6 +29,12 @@ struct AttnArgs {
   int waves;      // wavefronts per block (4 or 8): waves / hpb 32-token slices
   int tiles;      // token tiles
   float scale_log2;  // log2(e) / sqrt(hd)
+  // split-KV form: the keys of every (tile, head quad) are cut into kv_splits
+  // ranges whose unnormalised partial results go to po [split][M][nq][hd] and
+  // pml [split][M][nq][2] = (running max in log2 units, weight sum)
+  int kv_splits;
+  float* po;
+  float* pml;
 };
 
 // K and V blocks of 64 keys are copied global -> LDS with DMA into rings of
@@ -43,7 +49,7 @@ struct AttnArgs {
 // 4)) so the four rows x 64 bytes of a transposing step do.  Key rows past
 // the last visible key are clamped to it (finite data that the mask gives a
 // zero weight), so unwritten cache slots never reach the products.
-template <int HD, int NW>
+template <int HD, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int KB = 64;                 // keys per block
   constexpr int ROWB = HD * 2;           // bytes per key row
@@ -67,13 +73,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   const int hpb = a.hpb;
   const int tsub = NW / hpb;           // 32-token slices per block
   const int bt = 32 * tsub;            // tokens per block
-  // Work item w = (kv head j, head quad, tile), tile fastest and longest rows
-  // first.  Blocks are dealt round-robin to the eight XCDs, so block b is
-  // given item (b % 8) * (nb / 8) + b / 8: each XCD then works through a
-  // contiguous range of items, i.e. the tiles of one kv head, whose K/V
-  // blocks its L2 serves to all of them.
+  // Work item w = (kv head j, head quad, tile[, key range]), tile fastest
+  // (after the key range) and longest rows first.  Blocks are dealt
+  // round-robin to the eight XCDs, so block b is given item
+  // (b % 8) * (nb / 8) + b / 8: each XCD then works through a contiguous range
+  // of items, i.e. the tiles of one kv head, whose K/V blocks its L2 serves to
+  // all of them.
   const int nb = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
-  const int w = (nb & 7) ? b : (b & 7) * (nb >> 3) + (b >> 3);
+  const int w_all = (nb & 7) ? b : (b & 7) * (nb >> 3) + (b >> 3);
+  const int n_split = SPLIT ? a.kv_splits : 1;
+  const int split = w_all % n_split, w = w_all / n_split;
   const int tile = a.tiles - 1 - w % a.tiles;
   const int quads = a.group / hpb;
   const int jq = w / a.tiles;
@@ -101,6 +110,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   const int last_tok = min(a.M, (tile + 1) * bt) - 1;
   const int kv_end = a.start + last_tok + 1;          // keys this block may need
   const int nkb = (kv_end + KB - 1) / KB;
+  // key blocks [kb_lo, kb_hi) of this block (all of them unless split)
+  const int per = (nkb + n_split - 1) / n_split;
+  const int kb_lo = split * per;
+  const int kb_hi = min(nkb, kb_lo + per);
   const uint16_t* kbase = a.k + static_cast<size_t>(j) * a.max_seq * HD;
   const uint16_t* vbase = a.v + static_cast<size_t>(j) * a.max_seq * HD;
 
@@ -174,11 +187,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   const int tr_key = (lane & 15) >> 2;                       // + key base
   const int tr_dim = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;  // + 32*db
 
-  // prologue: K(0), V(0), K(1) in flight; scores of block 0 once K(0) landed
-  issue(0, false);
-  issue(0, true);
-  if (nkb > 1) {
-    issue(1, false);
+  if (SPLIT && kb_lo >= kb_hi) {   // an empty key range: a neutral partial result
+    if (q_ok) {
+      const size_t pr = (static_cast<size_t>(split) * a.M + t) * a.nq + h;
+      for (int d = lh; d < HD; d += 2) a.po[pr * HD + d] = 0.f;
+      if (lh == 0) {
+        a.pml[pr * 2] = -INFINITY;
+        a.pml[pr * 2 + 1] = 0.f;
+      }
+    }
+    return;
+  }
+
+  // prologue: K(lo), V(lo), K(lo+1) in flight; scores of block lo once K(lo) landed
+  issue(kb_lo, false);
+  issue(kb_lo, true);
+  if (kb_hi - kb_lo > 1) {
+    issue(kb_lo + 1, false);
     __builtin_amdgcn_s_waitcnt(VmWait<2 * PW>::imm);
   } else {
     __builtin_amdgcn_s_waitcnt(VmWait<PW>::imm);
@@ -191,8 +216,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
     const int key0 = kb * KB;
     __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wave's copies of V(kb), K(kb+1)
     lds_barrier();   // everyone's; V slot of kb-1 and K slot of kb-1 are free
-    if (kb + 1 < nkb) issue(kb + 1, true);
-    if (kb + 2 < nkb) issue(kb + 2, false);
+    if (kb + 1 < kb_hi) issue(kb + 1, true);
+    if (kb + 2 < kb_hi) issue(kb + 2, false);
     // the causal mask only cuts blocks that reach past the wave's first query
     if (key0 + KB - 1 > pos_lo) {
 #pragma unroll
@@ -224,8 +249,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
     // computed on the VALUs; the schedule below interleaves the two streams
     // (a wavefront issues in order).  The last iteration recomputes its own
     // block, whose K slot is still intact.
-    scores(min(kb + 1, nkb - 1), s_next);
-    const float neg_m = -m_run;
+    scores(min(kb + 1, kb_hi - 1), s_next);
+    // (a key range of the split form may hide every key from a row so far)
+    const float neg_m = SPLIT && m_run == -INFINITY ? 0.f : -m_run;
     bf16x8_t pf[4];   // B operand of step 2*hb + half: slots (lh, e) <- r = 8*half + e
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
@@ -273,16 +299,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   };
 
   f32x16_t sa[2], sb[2];
-  scores(0, sa);
-  int kb = 0;
-  for (; kb + 1 < nkb; kb += 2) {
+  scores(kb_lo, sa);
+  int kb = kb_lo;
+  for (; kb + 1 < kb_hi; kb += 2) {
     step(kb, sa, sb);
     step(kb + 1, sb, sa);
   }
-  if (kb < nkb) step(kb, sa, sb);
+  if (kb < kb_hi) step(kb, sa, sb);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!q_ok) return;
+  if constexpr (SPLIT) {
+    const size_t pr = (static_cast<size_t>(split) * a.M + t) * a.nq + h;
+    float* prow = a.po + pr * HD;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dd = d * 32 + r4 * 8 + lh * 4;
+        *reinterpret_cast<float4*>(prow + dd) = make_float4(
+            o[d][r4 * 4 + 0], o[d][r4 * 4 + 1], o[d][r4 * 4 + 2], o[d][r4 * 4 + 3]);
+      }
+    if (lh == 0) {
+      a.pml[pr * 2] = m_run;
+      a.pml[pr * 2 + 1] = l_tot;
+    }
+    return;
+  }
   const float inv = 1.0f / l_tot;
   uint16_t* orow = a.out + static_cast<size_t>(t) * a.out_ld + h * HD;
 #pragma unroll
@@ -295,6 +338,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
       w.y = pack_bf16x2(o[d][r4 * 4 + 2] * inv, o[d][r4 * 4 + 3] * inv);
       *reinterpret_cast<uint2*>(orow + dd) = w;
     }
+}
+
+// Merge of the split-KV partial results of one (query row, head): with M the
+// largest running max, o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+template <int HD>
+__global__ __launch_bounds__(HD) void attn_combine_kernel(const float* __restrict__ po,
+                                                         const float* __restrict__ pml,
+                                                         int n_split, int M, int nq,
+                                                         uint16_t* __restrict__ out, int out_ld) {
+  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  float m = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp)
+    m = fmaxf(m, pml[((static_cast<size_t>(sp) * M + t) * nq + h) * 2]);
+  float l = 0.f, acc = 0.f;
+  for (int sp = 0; sp < n_split; ++sp) {
+    const size_t pr = (static_cast<size_t>(sp) * M + t) * nq + h;
+    const float wgt = fast_exp2(pml[pr * 2] - m);
+    l += pml[pr * 2 + 1] * wgt;
+    acc += po[pr * HD + d] * wgt;
+  }
+  out[static_cast<size_t>(t) * out_ld + h * HD + d] = f32_to_bf16(acc / l);
 }
 
 // fp32 kernel: one block per (query token, query head); keys in chunks of
@@ -350,9 +414,46 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
   if (tid < hd) out[static_cast<size_t>(t) * out_ld + h * hd + tid] = acc / l_run;
 }
 
+// Blocks of the attention grid: (tiles, kv heads x head quads, waves) for M rows.
+struct AttnGrid {
+  int hpb, quads, waves, tiles, blocks;
+};
+static AttnGrid attn_grid(int M, int nq, int nkv) {
+  AttnGrid g{};
+  const int group = nq / nkv;
+  g.hpb = group < 4 ? group : 4;
+  g.quads = group / g.hpb;
+  // Eight wavefronts per block (one block per CU, K/V copied into LDS once per
+  // CU) when that still gives every CU a block; four (two blocks per CU)
+  // otherwise.
+  const int tiles8 = (M + 32 * (8 / g.hpb) - 1) / (32 * (8 / g.hpb));
+  g.waves = tiles8 * nkv * g.quads >= 256 ? 8 : 4;
+  const int bt = 32 * (g.waves / g.hpb);
+  g.tiles = (M + bt - 1) / bt;
+  g.blocks = g.tiles * nkv * g.quads;
+  return g;
+}
+
+int attention_kv_splits(int M, int kv_len, int nq, int nkv) {
+  const AttnGrid g = attn_grid(M, nq, nkv);
+  if (g.waves != 4 || g.blocks >= 256) return 1;   // the grid already fills the GPU
+  if (kv_len < 8 * M) return 1;   // keys mostly on the causal diagonal: ranges unbalanced
+  const int nkb = (kv_len + 63) / 64;
+  int ns = (512 + g.blocks - 1) / g.blocks;        // about 512 blocks in all
+  if (ns > kAttnMaxSplits) ns = kAttnMaxSplits;
+  if (ns > nkb / 4) ns = nkb / 4;                  // at least 4 key blocks per range
+  return ns < 2 ? 1 : ns;
+}
+
+size_t attention_split_floats(int M, int kv_len, int nq, int nkv, int head_dim) {
+  const int ns = attention_kv_splits(M, kv_len, nq, nkv);
+  return ns < 2 ? 0 : static_cast<size_t>(ns) * M * nq * (head_dim + 2);
+}
+
 hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_layer,
                             const void* v_layer, void* out, int out_ld, int M, int start,
-                            int nq, int nkv, int head_dim, int max_seq, hipStream_t s) {
+                            int nq, int nkv, int head_dim, int max_seq, float* split_ws,
+                            size_t split_ws_floats, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (act == Act::F32) {
     dim3 grid(M, nq);
@@ -362,6 +463,7 @@ hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_laye
         head_dim, max_seq, 1.0f / sqrtf(static_cast<float>(head_dim)));
     return hipGetLastError();
   }
+  const AttnGrid gr = attn_grid(M, nq, nkv);
   AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k_layer);
@@ -375,23 +477,37 @@ hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_laye
   a.nkv = nkv;
   a.max_seq = max_seq;
   a.group = nq / nkv;
-  a.hpb = a.group < 4 ? a.group : 4;
-  // Eight wavefronts per block (one block per CU, K/V copied into LDS once per
-  // CU) when that still gives every CU a block; four (two blocks per CU)
-  // otherwise.
-  const int quads = a.group / a.hpb;
-  const int tiles8 = (M + 32 * (8 / a.hpb) - 1) / (32 * (8 / a.hpb));
-  a.waves = tiles8 * nkv * quads >= 256 ? 8 : 4;
-  const int bt = 32 * (a.waves / a.hpb);
-  a.tiles = (M + bt - 1) / bt;
+  a.hpb = gr.hpb;
+  a.waves = gr.waves;
+  a.tiles = gr.tiles;
   a.scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
-  dim3 grid(a.tiles * nkv * quads);
+  a.kv_splits = 1;
+  const int ns = attention_kv_splits(M, start + M, nq, nkv);
+  if (ns > 1 && split_ws &&
+      static_cast<size_t>(ns) * M * nq * (head_dim + 2) <= split_ws_floats) {
+    // split-KV form: partial results per key range, then one merge pass
+    a.kv_splits = ns;
+    a.po = split_ws;
+    a.pml = split_ws + static_cast<size_t>(ns) * M * nq * head_dim;
+    dim3 grid(gr.blocks * ns);
+    if (head_dim == 128) attn_fwd_bf16_kernel<128, 4, true><<<grid, 256, 0, s>>>(a);
+    else attn_fwd_bf16_kernel<64, 4, true><<<grid, 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 cgrid(M, nq);
+    if (head_dim == 128)
+      attn_combine_kernel<128><<<cgrid, 128, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+    else
+      attn_combine_kernel<64><<<cgrid, 64, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+    return hipGetLastError();
+  }
+  dim3 grid(gr.blocks);
   if (head_dim == 128) {
-    if (a.waves == 8) attn_fwd_bf16_kernel<128, 8><<<grid, 512, 0, s>>>(a);
-    else attn_fwd_bf16_kernel<128, 4><<<grid, 256, 0, s>>>(a);
+    if (a.waves == 8) attn_fwd_bf16_kernel<128, 8, false><<<grid, 512, 0, s>>>(a);
+    else attn_fwd_bf16_kernel<128, 4, false><<<grid, 256, 0, s>>>(a);
   } else {
-    if (a.waves == 8) attn_fwd_bf16_kernel<64, 8><<<grid, 512, 0, s>>>(a);
-    else attn_fwd_bf16_kernel<64, 4><<<grid, 256, 0, s>>>(a);
+    if (a.waves == 8) attn_fwd_bf16_kernel<64, 8, false><<<grid, 512, 0, s>>>(a);
+    else attn_fwd_bf16_kernel<64, 4, false><<<grid, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -58,6 +58,22 @@ hipError_t launch_gemm(const GemmCall& c, hipStream_t s);
 // K slices the Partial epilogue uses for an M x N x K bf16 product (1 if not split).
 int gemm_partial_splits(int M, int N, int K);
 
+// ---- skinny-M projection (decode steps, verify rows) -----------------------
+// For M <= kSkinnyMaxM rows of bf16 A [M][lda] and dense bf16 W [N][K]: K is cut
+// into `splits` slices and slice s writes its fp32 product A W^T to
+// out + s * part_stride (row stride ldo); every slice is written, also an
+// empty one (zeros).  skinny_splits picks the slice count for an N x K weight.
+constexpr int kSkinnyMaxM = 32;
+constexpr int kSkinnyMaxSplits = 8;
+int skinny_splits(int N, int K);
+hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, int M, int N, int K,
+                              float* out, int ldo, size_t part_stride, int splits,
+                              hipStream_t s);
+// act[m][i] (bf16) = silu(g) * u with g, u the sums over `splits` fp32 slices of
+// the [M][2I] gate/up product (gate columns [0, I), up columns [I, 2I)).
+hipError_t launch_swiglu_finish(const float* part, int splits, size_t part_stride, int M, int I,
+                                void* act, hipStream_t s);
+
 // ---- QK-norm + RoPE + KV-cache store -----------------------------------------
 // Per token t (absolute position start + t): optional per-head RMSNorm of Q and K
 // heads, rotate-half RoPE of Q (written into qkv) and K, then K (roped) and V
@@ -74,9 +90,17 @@ hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const flo
 // ---- causal GQA attention ---------------------------------------------------
 // out[t][h*hd + d] for query rows t < M (roped Q at q + t*q_ld + h*hd) against
 // the cache slots [0, start + t] of kv head h / (nq / nkv).
+// When the (tile, head) grid alone would leave CUs idle (short micro-batches
+// over long caches) and split_ws holds attention_split_floats(M, start + M, ..)
+// floats, the keys are cut into ranges whose partial results (max, weight sum,
+// unnormalised output) a second pass merges.
+constexpr int kAttnMaxSplits = 64;
+int attention_kv_splits(int M, int kv_len, int nq, int nkv);
+size_t attention_split_floats(int M, int kv_len, int nq, int nkv, int head_dim);
 hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_layer,
                             const void* v_layer, void* out, int out_ld, int M, int start,
-                            int nq, int nkv, int head_dim, int max_seq, hipStream_t s);
+                            int nq, int nkv, int head_dim, int max_seq, float* split_ws,
+                            size_t split_ws_floats, hipStream_t s);
 
 // ---- last-token head --------------------------------------------------------
 // logits[v] = sum_k W[v][k] * xn[k] with xn fp32 [H] and W [V][H] in act type.

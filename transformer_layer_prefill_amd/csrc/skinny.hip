@@ -1,0 +1,165 @@
+// Projections of short micro-batches (M <= 32 token rows): the decode steps
+// of a token-by-token forward (oxibonsai-kernels metal_full_layer.rs, the
+// per-token layer: the same projections applied to one hidden row) and the
+// rows of a speculative verify batch.  At these sizes a projection reads each
+// weight once and does little arithmetic per byte, so it is bound by HBM
+// bandwidth; the 256x256 prefill tiles would waste almost all of their MFMA
+// work on padding rows.
+//
+// Every wavefront multiplies 32 weight rows by all M activation rows,
+// zero-padded to the 32 columns of v_mfma_f32_32x32x16_bf16, over one slice
+// of K.  The weight rows stream from HBM straight into registers: lane
+// (row r, half h) loads the 16-byte chunks 2s + h of the row's 128-byte
+// lines, so the two lanes of a row consume whole lines.  The products are
+// written as fp32 split-K slices that the following row kernel sums (or the
+// SwiGLU finish below, for the fused gate/up weight).
+#include "common.h"
+#include "launch.h"
+
+namespace tlp {
+
+struct SkinnyArgs {
+  const uint16_t* A;     // [M][lda] bf16
+  const uint16_t* W;     // [N][K] bf16
+  float* out;            // slice s at out + s * part_stride, [M][ldo] fp32
+  size_t part_stride;
+  int lda, ldo;
+  int M, N, K;
+  int splits, k_split;   // k_split: a multiple of 64
+  int groups;            // ceil(N / 32)
+};
+
+__device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ bf16x8_t zero16() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
+
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
+  constexpr int STEPS = 16;   // 16-wide k-steps per main-loop iteration (256 of K)
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= g.groups * g.splits) return;   // whole wavefronts
+  const int split = item % g.splits, grp = item / g.splits;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int n = grp * 32 + lr;
+  const uint16_t* wrow = g.W + static_cast<size_t>(n < g.N ? n : g.N - 1) * g.K + 8 * lh;
+  const bool a_ok = lr < g.M;
+  const uint16_t* arow = g.A + static_cast<size_t>(a_ok ? lr : 0) * g.lda + 8 * lh;
+  const int k_begin = split * g.k_split;
+  const int k_end = min(g.K, k_begin + g.k_split);
+
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+
+  int k = k_begin;
+  for (; k + 16 * STEPS <= k_end; k += 16 * STEPS) {
+    bf16x8_t wv[STEPS], av[STEPS];
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) wv[j] = ld16(wrow + k + 16 * j);
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) av[j] = a_ok ? ld16(arow + k + 16 * j) : zero16();
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[j], av[j], acc, 0, 0, 0);
+  }
+  for (; k + 64 <= k_end; k += 64) {
+    bf16x8_t wv[4], av[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wv[j] = ld16(wrow + k + 16 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) av[j] = a_ok ? ld16(arow + k + 16 * j) : zero16();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[j], av[j], acc, 0, 0, 0);
+  }
+  // remaining 16-wide steps; a half step past K (K % 16 == 8) reads zeros
+  for (; k < k_end; k += 16) {
+    const bool ok = k + 8 * lh < k_end;
+    const bf16x8_t wv = ok ? ld16(wrow + k) : zero16();
+    const bf16x8_t av = ok && a_ok ? ld16(arow + k) : zero16();
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, av, acc, 0, 0, 0);
+  }
+
+  // lane holds output column m = lr and weight rows grp*32 + 8*(r/4) + 4*lh + r%4
+  if (!a_ok) return;
+  float* orow = g.out + split * g.part_stride + static_cast<size_t>(lr) * g.ldo;
+  const bool vec = ((g.ldo | g.part_stride) & 3) == 0;   // float4-aligned rows
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int n0 = grp * 32 + 8 * q + 4 * lh;
+    if (vec && n0 + 3 < g.N) {
+      *reinterpret_cast<float4*>(orow + n0) =
+          make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n0 + i < g.N) orow[n0 + i] = acc[4 * q + i];
+    }
+  }
+}
+
+int skinny_splits(int N, int K) {
+  const int groups = (N + 31) / 32;
+  int splits = (2048 + groups - 1) / groups;   // ~8 wavefronts per CU
+  if (splits > kSkinnyMaxSplits) splits = kSkinnyMaxSplits;
+  const int max_by_k = K / 256;                 // slices of at least 256
+  if (splits > max_by_k) splits = max_by_k;
+  return splits < 1 ? 1 : splits;
+}
+
+hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, int M, int N, int K,
+                              float* out, int ldo, size_t part_stride, int splits,
+                              hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (M > kSkinnyMaxM || splits < 1 || (K & 7) || (lda & 7)) return hipErrorInvalidValue;
+  SkinnyArgs g{};
+  g.A = static_cast<const uint16_t*>(A);
+  g.W = static_cast<const uint16_t*>(W);
+  g.out = out;
+  g.part_stride = part_stride;
+  g.lda = lda;
+  g.ldo = ldo;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.splits = splits;
+  // slices of whole 256-wide main-loop iterations when K allows (the last
+  // slice may be shorter, or empty: it then writes zeros)
+  const int gran = K >= 256 * splits ? 256 : 64;
+  g.k_split = ((K + splits - 1) / splits + gran - 1) / gran * gran;
+  g.groups = (N + 31) / 32;
+  const int waves = g.groups * splits;
+  gemm_skinny_kernel<<<(waves + 3) / 4, 256, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+// act[m][i] = silu(gate) * up with gate = sum_s part_s[m][i] and up =
+// sum_s part_s[m][I + i] (the fused [gate ; up] weight's slices).
+__global__ __launch_bounds__(256) void swiglu_finish_kernel(const float* __restrict__ part,
+                                                            int splits, size_t part_stride,
+                                                            int M, int I,
+                                                            uint16_t* __restrict__ act) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<size_t>(M) * I) return;
+  const int m = static_cast<int>(idx / I), i = static_cast<int>(idx % I);
+  const float* p = part + static_cast<size_t>(m) * 2 * I + i;
+  float gsum = 0.f, usum = 0.f;
+  for (int sl = 0; sl < splits; ++sl) {
+    gsum += p[sl * part_stride];
+    usum += p[sl * part_stride + I];
+  }
+  act[idx] = f32_to_bf16(silu_f32(gsum) * usum);
+}
+
+hipError_t launch_swiglu_finish(const float* part, int splits, size_t part_stride, int M, int I,
+                                void* act, hipStream_t s) {
+  if (M <= 0 || I <= 0) return hipSuccess;
+  const size_t n = static_cast<size_t>(M) * I;
+  swiglu_finish_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+      part, splits, part_stride, M, I, static_cast<uint16_t*>(act));
+  return hipGetLastError();
+}
+
+}  // namespace tlp
