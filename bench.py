@@ -139,6 +139,63 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4}))
 
 
+def bench_verify_tail(args):
+    """Speculative-verify tail of the Llama-3-8B head: final RMSNorm of 16 rows,
+    LM-head projection to 128256 fp32 logits per row, per-row argmax.  HBM
+    bound: the 1.05 GB head is read once per call."""
+    import torch
+    import transformer_layer_prefill_amd as tlp
+    from transformer_layer_prefill_amd import tensors
+    rows, H, V = 16, 4096, 128256
+    sh = synth.Shape("llama3-8b-verify-tail", hidden=H, inter=14336, nq=32, nkv=8,
+                     head_dim=128, qk_norm=False, eps=1e-5, theta=5e5, n_tokens=rows,
+                     start=0, max_seq=4096, vocab=V, seed=1004)
+    log("[bench] generating the 128256 x 4096 head")
+    x = tensors.to_device(synth.hidden_input(sh))
+    g = tensors.to_device(synth.final_norm(sh))
+    W = tensors.to_device(synth.lm_head(sh, workers=16))
+    cfg = tensors.config_of(sh)
+    logits = torch.empty((rows, V), dtype=torch.float32, device="cuda")
+    tokens = torch.empty(rows, dtype=torch.int32, device="cuda")
+    ws = torch.empty(tlp.verify_workspace_bytes(cfg, rows), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        tlp.verify_tail(cfg, x, rows, g, W, V, sh.eps, logits, tokens, ws, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tlp.profile_begin()
+    for _ in range(args.steps):
+        step()
+    prof = tlp.profile_end()
+    kernels = {k: {"launches": n, "avg_us": round(1e3 * t / n, 3)} for k, (n, t) in prof.items() if n}
+    head_us = kernels["lm_head"]["avg_us"]
+    head_bytes = 2 * V * H + 2 * rows * H + 4 * rows * V
+    achieved = head_bytes / (head_us * 1e-6) / 1e9
+    out = {
+        "metric": "verify-tail rows/sec (final norm + LM head + argmax)", "value": round(rows / (ms * 1e-3), 1),
+        "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": sh.name, "rows": rows, "hidden": H, "vocab": V,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "lm_head", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "avg_us": head_us, "bytes_per_launch": head_bytes},
+        "cpu_baseline": None,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,7 +203,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3-8b-layer",
                     choices=["llama3-8b-layer", "qwen3-8b-sign1-layer", "llama3-8b-long-ctx",
-                             "llama3-8b-decode", "llama3-8b-long-decode"])
+                             "llama3-8b-decode", "llama3-8b-long-decode",
+                             "llama3-8b-verify-tail"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times "
@@ -160,6 +218,10 @@ def main():
               "sharding of this path is a design in DESIGN.md, not a measured run",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "llama3-8b-verify-tail":
+        bench_verify_tail(args)
+        return
 
     import torch
     import transformer_layer_prefill_amd as tlp

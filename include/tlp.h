@@ -169,6 +169,36 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
                              float final_eps, float* logits, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Greedy token choice (prefill page, encode_full_forward_prefill: the greedy
+ * branch of the tail runs an argmax over the logits on the GPU and returns a
+ * 4-byte token id instead of the logits).  token_ids[r] = the lowest index v
+ * in [0, vocab) whose logits[r * ld + v] is maximal, compared in fp32; NaN
+ * entries are never chosen and a row with no entry above -inf gives 0.
+ * logits: device fp32 [rows][ld] with ld >= vocab; token_ids: device int32
+ * [rows].  rows > 0, vocab > 0 (TLP_ERR_SHAPE otherwise). */
+tlp_status tlp_argmax_rows(const float* logits, int32_t rows, int32_t vocab, int64_t ld,
+                           int32_t* token_ids, void* stream);
+
+/* Workspace bytes tlp_verify_tail needs for up to n_rows rows (0 if the
+ * config is invalid or n_rows <= 0). */
+size_t tlp_verify_workspace_bytes(const tlp_config* cfg, int32_t n_rows);
+
+/* Speculative-decode verify tail (prefill page,
+ * encode_full_forward_prefill_verify, its tail: final RMSNorm and LM head on
+ * every batch position, then a per-position argmax).  For each row r of
+ * hidden [n_rows][H] (dtype; e.g. the rows tlp_prefill_chunk wrote):
+ *   logits[r][v] = sum_k lm_head[v][k] * RMSNorm(hidden[r]; final_norm, final_eps)[k]
+ *   token_ids[r] = tlp_argmax_rows of logits row r   (if token_ids is not NULL)
+ * lm_head [vocab][H] and final_norm [H] in dtype, 16-byte aligned; logits
+ * device fp32 [n_rows][vocab], 16-byte aligned, required (the product is
+ * written there); token_ids device int32 [n_rows] or NULL.  The config's
+ * layer fields other than hidden, dtype and rms limits are not used.
+ * workspace >= tlp_verify_workspace_bytes(cfg, n_rows), 256-byte aligned. */
+tlp_status tlp_verify_tail(const tlp_config* cfg, const void* hidden, int32_t n_rows,
+                           const void* final_norm, const void* lm_head, int32_t vocab,
+                           float final_eps, float* logits, int32_t* token_ids, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Kernels as timed by the profiler below. */
 enum { TLP_K_ATTN_NORM = 0, TLP_K_QKV_GEMM = 1, TLP_K_QK_ROPE_KV = 2, TLP_K_ATTENTION = 3,
        TLP_K_O_GEMM = 4, TLP_K_FFN_NORM = 5, TLP_K_GATE_UP_GEMM = 6, TLP_K_DOWN_GEMM = 7,

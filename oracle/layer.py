@@ -223,6 +223,28 @@ def lm_head_logits(x_last: np.ndarray, final_gain: np.ndarray, eps: float,
     return as_dense(head) @ rms_norm(x_last, final_gain, eps)
 
 
+def argmax_rows(logits: np.ndarray) -> np.ndarray:
+    """Greedy token per row: the first index of the row's largest logit.
+
+    Prefill page, ``encode_full_forward_prefill``: the greedy branch of the
+    tail runs an argmax over the logits on the GPU and hands back one token id.
+    The kernel body is not on the pages; ties go to the lowest index (the
+    reading taken here), which is what ``numpy.argmax`` returns.
+    """
+    return np.argmax(np.asarray(logits), axis=-1)
+
+
+def verify_tail(x_rows: np.ndarray, final_gain: np.ndarray, eps: float, head: np.ndarray):
+    """Speculative-verify tail: ``(logits, token ids)`` of every row.
+
+    Prefill page, ``encode_full_forward_prefill_verify``: its tail runs the
+    final RMSNorm over all batch positions, the LM-head GEMM on the normed
+    rows, then one argmax per position.  Each row is normed on its own.
+    """
+    logits = rms_norm(np.asarray(x_rows), final_gain, eps) @ as_dense(head).T
+    return logits, argmax_rows(logits)
+
+
 def prefill_chunk(shape, layers: list, x: np.ndarray, start: int, micro_batch: int,
                   k_cache: np.ndarray, v_cache: np.ndarray,
                   final_gain: np.ndarray | None = None, head=None,

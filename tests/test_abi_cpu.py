@@ -127,6 +127,33 @@ def test_chunk_argument_checks():
     assert chunk(layers=bad) == tlp.TLP_ERR_NULL
 
 
+def test_argmax_and_verify_argument_checks():
+    L = tlp.lib()
+    assert L.tlp_argmax_rows(None, 2, 10, 10, FAKE, None) == tlp.TLP_ERR_NULL
+    assert L.tlp_argmax_rows(FAKE, 2, 10, 10, None, None) == tlp.TLP_ERR_NULL
+    assert L.tlp_argmax_rows(FAKE, 0, 10, 10, FAKE, None) == tlp.TLP_ERR_SHAPE
+    assert L.tlp_argmax_rows(FAKE, 2, 0, 10, FAKE, None) == tlp.TLP_ERR_SHAPE
+    assert L.tlp_argmax_rows(FAKE, 2, 10, 9, FAKE, None) == tlp.TLP_ERR_SHAPE
+    cfg = _cfg()
+    assert tlp.verify_workspace_bytes(cfg, 0) == 0
+    assert tlp.verify_workspace_bytes(cfg, 3) == 1536   # bf16 [3][256], 256-byte multiple
+    wsb = tlp.verify_workspace_bytes(cfg, 3)
+
+    def verify(n=3, norm=FAKE, head=FAKE, vocab=10, logits=FAKE, ws=FAKE, wsb=wsb, eps=1e-5):
+        return L.tlp_verify_tail(ctypes.byref(cfg), FAKE, n, norm, head, vocab, eps, logits,
+                                 None, ws, wsb, None)
+
+    assert verify(head=None) == tlp.TLP_ERR_NULL
+    assert verify(norm=None) == tlp.TLP_ERR_NULL
+    assert verify(logits=None) == tlp.TLP_ERR_NULL
+    assert verify(n=0) == tlp.TLP_ERR_SHAPE
+    assert verify(vocab=0) == tlp.TLP_ERR_SHAPE
+    assert verify(eps=-1.0) == tlp.TLP_ERR_SHAPE
+    assert verify(logits=FAKE + 4) == tlp.TLP_ERR_UNSUPPORTED
+    assert verify(ws=FAKE + 16) == tlp.TLP_ERR_UNSUPPORTED
+    assert verify(wsb=wsb - 1) == tlp.TLP_ERR_WORKSPACE
+
+
 def test_workspace_sizes():
     cfg = _cfg()
     assert tlp.workspace_bytes(cfg, 0) == 0

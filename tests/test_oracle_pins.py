@@ -406,3 +406,42 @@ def test_chunk_head_runs_on_final_token_of_last_micro_batch():
                                        head=np.eye(sh.hidden), final_eps=0.0)
     last = out[-1]
     np.testing.assert_allclose(logits, last / math.sqrt(np.mean(last ** 2)), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- greedy argmax and verify tail
+
+@pytest.mark.parametrize("case", _golden()["argmax"])
+def test_argmax_hand_cases(case):
+    logits = np.array([float(v) for v in case["logits"]], dtype=np.float64)
+    assert int(oracle.argmax_rows(logits)) == case["expected"]
+
+
+def test_argmax_rows_is_per_row_and_brute_force():
+    rng = np.random.default_rng(5)
+    x = rng.integers(-3, 4, size=(9, 13)).astype(np.float64)   # many ties
+    got = oracle.argmax_rows(x)
+    for r in range(x.shape[0]):
+        best = max(x[r])
+        assert got[r] == min(v for v in range(x.shape[1]) if x[r, v] == best)
+
+
+@pytest.mark.parametrize("case", _golden()["verify_tail"])
+def test_verify_tail_hand_cases(case):
+    logits, tokens = oracle.verify_tail(np.array(case["x"]), np.array(case["gain"]),
+                                        case["eps"], np.array(case["head"]))
+    exp = np.array([_eval(row) for row in case["expected_logits"]])
+    np.testing.assert_allclose(logits, exp, rtol=1e-15, atol=1e-15)
+    assert tokens.tolist() == case["expected_tokens"]
+
+
+def test_verify_tail_rows_are_normed_independently():
+    # at eps = 0 a row's logits do not change when the row is scaled, whatever
+    # the other rows hold; a norm over the batch (or over columns) would
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((3, 8))
+    W = rng.standard_normal((5, 8))
+    g = 1 + 0.1 * rng.standard_normal(8)
+    base, _ = oracle.verify_tail(x, g, 0.0, W)
+    scaled = x * np.array([[1.0], [7.0], [0.25]])
+    got, _ = oracle.verify_tail(scaled, g, 0.0, W)
+    np.testing.assert_allclose(got, base, rtol=1e-12)

@@ -20,8 +20,9 @@ TLP_W_DENSE, TLP_W_SIGN1_G128 = 0, 1
 WS_RES, WS_XN, WS_QKV, WS_ATTN, WS_ACT, WS_HEAD, WS_PART, WS_COUNT = range(8)
 
 EXPORTS = ("tlp_workspace_bytes", "tlp_workspace_layout", "tlp_rope_table",
-           "tlp_prefill_layer", "tlp_prefill_chunk", "tlp_profile_begin", "tlp_profile_end",
-           "tlp_status_string", "tlp_last_error")
+           "tlp_prefill_layer", "tlp_prefill_chunk", "tlp_argmax_rows",
+           "tlp_verify_workspace_bytes", "tlp_verify_tail", "tlp_profile_begin",
+           "tlp_profile_end", "tlp_status_string", "tlp_last_error")
 KERNELS = ("attn_norm", "qkv_gemm", "qk_rope_kv", "attention", "o_gemm", "ffn_norm",
            "gate_up_gemm", "down_gemm", "final_norm", "lm_head", "out_rows", "swiglu",
            "argmax")
@@ -78,6 +79,13 @@ def lib() -> ctypes.CDLL:
                                         vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz,
                                         vp]
         L.tlp_prefill_chunk.restype = ctypes.c_int
+        L.tlp_argmax_rows.argtypes = [vp, i32, i32, ctypes.c_int64, vp, vp]
+        L.tlp_argmax_rows.restype = ctypes.c_int
+        L.tlp_verify_workspace_bytes.argtypes = [cfgp, i32]
+        L.tlp_verify_workspace_bytes.restype = sz
+        L.tlp_verify_tail.argtypes = [cfgp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp,
+                                      sz, vp]
+        L.tlp_verify_tail.restype = ctypes.c_int
         L.tlp_profile_begin.argtypes = []
         L.tlp_profile_begin.restype = ctypes.c_int
         L.tlp_profile_end.argtypes = [vp, vp]
@@ -161,6 +169,25 @@ def prefill_chunk(cfg: Config, layers, hidden, n_tokens: int, start_position: in
                                    _ptr(rope_cos), _ptr(rope_sin), _ptr(final_norm),
                                    _ptr(lm_head), vocab, final_eps, _ptr(logits),
                                    _ptr(workspace), wsb, _stream(stream)))
+
+
+def argmax_rows(logits, rows: int, vocab: int, ld: int, token_ids, stream=None) -> None:
+    _check(lib().tlp_argmax_rows(_ptr(logits), rows, vocab, ld, _ptr(token_ids),
+                                 _stream(stream)))
+
+
+def verify_workspace_bytes(cfg: Config, n_rows: int) -> int:
+    return int(lib().tlp_verify_workspace_bytes(ctypes.byref(cfg), n_rows))
+
+
+def verify_tail(cfg: Config, hidden, n_rows: int, final_norm, lm_head, vocab: int,
+                final_eps: float, logits, token_ids, workspace,
+                workspace_bytes: int | None = None, stream=None) -> None:
+    wsb = workspace_bytes if workspace_bytes is not None else \
+        workspace.numel() * workspace.element_size()
+    _check(lib().tlp_verify_tail(ctypes.byref(cfg), _ptr(hidden), n_rows, _ptr(final_norm),
+                                 _ptr(lm_head), vocab, final_eps, _ptr(logits),
+                                 _ptr(token_ids), _ptr(workspace), wsb, _stream(stream)))
 
 
 def profile_begin() -> None:

@@ -499,6 +499,73 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
   return TLP_OK;
 }
 
+tlp_status tlp_argmax_rows(const float* logits, int32_t rows, int32_t vocab, int64_t ld,
+                           int32_t* token_ids, void* stream) {
+  if (!logits || !token_ids) return fail(TLP_ERR_NULL, "logits and token_ids are required");
+  if (rows <= 0 || vocab <= 0) return fail(TLP_ERR_SHAPE, "rows %d and vocab %d must be > 0",
+                                           rows, vocab);
+  if (ld < vocab) return fail(TLP_ERR_SHAPE, "ld %lld below vocab %d",
+                              static_cast<long long>(ld), vocab);
+  g_last_error.clear();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TLP_LAUNCH(TLP_K_ARGMAX, tlp::launch_argmax_rows(logits, rows, vocab, static_cast<size_t>(ld),
+                                                   token_ids, s));
+  return TLP_OK;
+}
+
+size_t tlp_verify_workspace_bytes(const tlp_config* cfg, int32_t n_rows) {
+  if (check_config(cfg) != TLP_OK || n_rows <= 0) return 0;
+  return align256(static_cast<size_t>(n_rows) * cfg->hidden * elt_size(*cfg));
+}
+
+tlp_status tlp_verify_tail(const tlp_config* cfg, const void* hidden, int32_t n_rows,
+                           const void* final_norm, const void* lm_head, int32_t vocab,
+                           float final_eps, float* logits, int32_t* token_ids, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  tlp_status st = check_config(cfg);
+  if (st != TLP_OK) return st;
+  if (!hidden || !final_norm || !lm_head || !logits || !workspace)
+    return fail(TLP_ERR_NULL, "hidden, final_norm, lm_head, logits and workspace are required");
+  if (n_rows <= 0 || vocab <= 0)
+    return fail(TLP_ERR_SHAPE, "n_rows %d and vocab %d must be > 0", n_rows, vocab);
+  if (!(final_eps >= 0.f) || !std::isfinite(final_eps))
+    return fail(TLP_ERR_SHAPE, "final_eps must be finite and >= 0");
+  if (!aligned16(hidden) || !aligned16(final_norm) || !aligned16(lm_head) || !aligned16(logits))
+    return fail(TLP_ERR_UNSUPPORTED, "hidden, final_norm, lm_head and logits must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(TLP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const size_t need = tlp_verify_workspace_bytes(cfg, n_rows);
+  if (workspace_bytes < need)
+    return fail(TLP_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  using namespace tlp;
+  const Act act = cfg->dtype == TLP_F32 ? Act::F32 : Act::BF16;
+  const int H = cfg->hidden;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  g_last_error.clear();
+  // final RMSNorm of every row
+  RowArgs r{};
+  r.x = hidden; r.x_f32 = 0; r.ldx = H;
+  r.gain = final_norm; r.norm_out = workspace; r.norm_f32 = 0;
+  r.rows = n_rows; r.H = H; r.eps = final_eps;
+  TLP_LAUNCH(TLP_K_FINAL_NORM, launch_rownorm(act, r, s));
+  // LM head: fp32 logits [n_rows][vocab]
+  if (act == Act::BF16 && n_rows <= kSkinnyMaxM) {
+    TLP_LAUNCH(TLP_K_LM_HEAD, launch_gemm_skinny(workspace, H, lm_head, n_rows, vocab, H, logits,
+                                                 vocab, 0, 1, s));
+  } else {
+    GemmCall g{};
+    g.act = act;
+    g.A = workspace; g.lda = H;
+    g.W = lm_head;
+    g.M = n_rows; g.N = vocab; g.K = H;
+    g.epi = Epi::StoreF32; g.out = logits; g.ldo = vocab; g.out_f32 = true;
+    TLP_LAUNCH(TLP_K_LM_HEAD, launch_gemm(g, s));
+  }
+  if (token_ids)
+    TLP_LAUNCH(TLP_K_ARGMAX, launch_argmax_rows(logits, n_rows, vocab, vocab, token_ids, s));
+  return TLP_OK;
+}
+
 tlp_status tlp_profile_begin(void) {
   for (auto& r : g_prof) {
     g_event_pool.push_back(r.start);

@@ -562,9 +562,18 @@ static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
   return run_bf16<128, 128, 2, 2, EPI, SIGN1, OUT_F32>(g, 1, s);
 }
 
+// fp32 output in one pass: the slice writer with a single slice
+template <bool SIGN1>
+static hipError_t pick_store_f32(GemmArgs g, hipStream_t s) {
+  const long tiles_big = static_cast<long>((g.M + 255) / 256) * ((g.N + 255) / 256);
+  if (tiles_big >= kCUs * 3 / 4) return run_bf16<256, 256, 2, 4, 4, SIGN1, true>(g, 1, s);
+  return run_bf16<128, 128, 2, 2, 4, SIGN1, true>(g, 1, s);
+}
+
 template <bool SIGN1>
 static hipError_t dispatch_bf16(const GemmCall& c, GemmArgs g, hipStream_t s) {
   switch (c.epi) {
+    case Epi::StoreF32: return pick_store_f32<SIGN1>(g, s);
     case Epi::Store: return pick_bf16<0, SIGN1, false>(g, s);
     case Epi::SwiGLU: return pick_bf16<2, SIGN1, false>(g, s);
     case Epi::Partial: return pick_bf16<4, SIGN1, true>(g, s);
@@ -598,7 +607,8 @@ hipError_t launch_gemm(const GemmCall& c, hipStream_t s) {
     g.n_tiles = (c.N + cols - 1) / cols;
     const int blocks = g.m_tiles * g.n_tiles;
     switch (c.epi) {
-      case Epi::Store: gemm_f32_kernel<0><<<blocks, 256, 0, s>>>(g); break;
+      case Epi::Store:
+      case Epi::StoreF32: gemm_f32_kernel<0><<<blocks, 256, 0, s>>>(g); break;
       case Epi::Resid: gemm_f32_kernel<1><<<blocks, 256, 0, s>>>(g); break;
       case Epi::SwiGLU: gemm_f32_kernel<2><<<blocks, 256, 0, s>>>(g); break;
       case Epi::Partial: return hipErrorInvalidValue;

@@ -35,7 +35,8 @@ hipError_t launch_rownorm(Act act, const RowArgs& a, hipStream_t s);
 // silu(gate_j) * up_j with gate rows [0, N) and up rows [N, 2N) of W.
 // Partial: K is split into `splits` slices; slice s writes its fp32 product to
 // part + s * part_stride (row stride ldo) for a later row pass to sum (bf16 only).
-enum class Epi { Store = 0, Resid = 1, SwiGLU = 2, Partial = 4 };
+// StoreF32: out = A W^T as fp32 [M][ldo] in one pass (no K split).
+enum class Epi { Store = 0, Resid = 1, SwiGLU = 2, Partial = 4, StoreF32 = 5 };
 struct GemmCall {
   Act act;             // A, W (dense) and Store/SwiGLU outputs use this type
   const void* A;       // [M][K], row stride lda
@@ -106,6 +107,11 @@ hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_laye
 // logits[v] = sum_k W[v][k] * xn[k] with xn fp32 [H] and W [V][H] in act type.
 hipError_t launch_lm_head(Act act, const float* xn, const void* W, float* logits, int V, int H,
                           hipStream_t s);
+
+// ---- greedy token choice ------------------------------------------------------
+// out[r] = the lowest index v < vocab with logits[r * ld + v] maximal.
+hipError_t launch_argmax_rows(const float* logits, int rows, int vocab, size_t ld, int32_t* out,
+                              hipStream_t s);
 
 
 }  // namespace tlp
