@@ -206,6 +206,8 @@ def main():
                              "llama3-8b-decode", "llama3-8b-long-decode",
                              "llama3-8b-verify-tail"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-f16", action="store_true",
+                    help="keep the KV cache in IEEE fp16 (the pages' cache type)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times "
                          "(the calibration kernel for HBM traffic counters), then exit")
@@ -228,6 +230,8 @@ def main():
     from transformer_layer_prefill_amd import tensors
 
     sh = synth.WORKLOADS[args.workload]
+    if args.kv_f16:
+        sh = sh.replace(kv="f16")
     log(f"[bench] generating {sh.name}")
     w = synth.layer_weights(sh, 0)
     x = synth.hidden_input(sh)
@@ -339,6 +343,7 @@ def main():
         "config": {"workload": sh.name, "tokens": sh.n_tokens, "start_position": sh.start,
                    "hidden": sh.hidden, "intermediate": sh.inter, "q_heads": sh.nq,
                    "kv_heads": sh.nkv, "head_dim": sh.head_dim, "weights": sh.wformat,
+                   "kv_cache": sh.kv_dtype,
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,

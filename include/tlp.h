@@ -65,6 +65,13 @@ typedef enum { TLP_F32 = 0, TLP_BF16 = 1 } tlp_dtype;
  *   Requires K % 128 == 0 and dtype TLP_BF16. */
 typedef enum { TLP_W_DENSE = 0, TLP_W_SIGN1_G128 = 1 } tlp_wformat;
 
+/* KV-cache element format.
+ * TLP_KV_ACT: the cache holds K and V in the config's dtype.
+ * TLP_KV_F16: IEEE fp16 (the cache type of the layer page's GpuKvCache and of
+ *   the chunk page's attention), rounded to nearest-even when stored; needs
+ *   dtype TLP_BF16.  Values beyond the fp16 range become +-inf. */
+typedef enum { TLP_KV_ACT = 0, TLP_KV_F16 = 1 } tlp_kv_format;
+
 typedef struct {
   int32_t hidden;       /* H; multiple of 8, at most 16384 */
   int32_t intermediate; /* I; multiple of 8 */
@@ -77,6 +84,7 @@ typedef struct {
   int32_t qk_norm;      /* non-zero: per-head RMSNorm of Q and K before RoPE */
   int32_t dtype;        /* tlp_dtype */
   int32_t wformat;      /* tlp_wformat */
+  int32_t kv_format;    /* tlp_kv_format (0: caches in dtype) */
 } tlp_config;
 
 /* One projection weight.  Dense: data = [N][K], scales = NULL.
@@ -138,7 +146,7 @@ tlp_status tlp_rope_table(double theta, int32_t head_dim, int32_t n_pos, float* 
  *   6 a = silu(W_gate x_n2) * (W_up x_n2)   7 x += W_down a
  * hidden: [n_tokens][H] in dtype, read and overwritten in place.  The residual
  * stream inside the call is fp32.  k_cache, v_cache: [n_layers][nkv][max_seq][hd]
- * in dtype; exactly the slots [start_position, start_position + n_tokens) of
+ * in dtype (fp16 with TLP_KV_F16); exactly the slots [start_position, start_position + n_tokens) of
  * `layer` are written, slots [0, start_position + n_tokens) of `layer` are read,
  * and every slot below start_position must already hold that position's K/V.
  * rope_cos, rope_sin: device fp32 [>= start_position + n_tokens][hd/2].

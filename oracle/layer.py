@@ -173,6 +173,20 @@ def qkv_rows(shape, w: dict, x: np.ndarray, positions: np.ndarray):
     return q, k, v
 
 
+def cache_store(shape, kv: np.ndarray) -> np.ndarray:
+    """Values as a KV cache of the shape's format holds them.
+
+    The layer page's ``GpuKvCache`` and the chunk page's attention keep K and
+    V in f16; with that format (``shape.kv == "f16"``) a stored value is the
+    nearest IEEE half (ties to even, numpy's conversion), so later attention
+    reads the rounded value.  Otherwise the cache is exact here.
+    """
+    if getattr(shape, "kv", "act") == "f16":
+        with np.errstate(over="ignore"):    # beyond the half range is +-inf by definition
+            return np.asarray(kv, dtype=np.float64).astype(np.float16).astype(np.float64)
+    return kv
+
+
 def prefill_layer(shape, w: dict, layer: int, x: np.ndarray, start: int,
                   k_cache: np.ndarray, v_cache: np.ndarray,
                   rows: np.ndarray | None = None) -> np.ndarray:
@@ -199,8 +213,8 @@ def prefill_layer(shape, w: dict, layer: int, x: np.ndarray, start: int,
     n = x.shape[0]
     positions = start + np.arange(n)
     q, k, v = qkv_rows(shape, w, x, positions)
-    k_cache[layer][:, start:start + n, :] = k.transpose(1, 0, 2)
-    v_cache[layer][:, start:start + n, :] = v.transpose(1, 0, 2)
+    k_cache[layer][:, start:start + n, :] = cache_store(shape, k.transpose(1, 0, 2))
+    v_cache[layer][:, start:start + n, :] = cache_store(shape, v.transpose(1, 0, 2))
     if rows is None:
         rows = np.arange(n)
     attn = causal_gqa_attention(q[rows], k_cache[layer], v_cache[layer], positions[rows])

@@ -35,9 +35,10 @@ import numpy as np
 
 SIGN1_GROUP = 128
 
-# fp32 / bf16 NaN patterns that mark cache slots no call has written.
+# fp32 / bf16 / fp16 NaN patterns that mark cache slots no call has written.
 SENTINEL_F32 = np.uint32(0x7FC0DEAD)
 SENTINEL_BF16 = np.uint16(0x7FDE)
+SENTINEL_F16 = np.uint16(0x7E5A)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,6 +63,7 @@ class Shape:
     micro_batch: int = 0         # 0: one micro-batch holds every token
     vocab: int = 0               # 0: no LM head
     seed: int = 1000
+    kv: str = "act"              # KV-cache format: "act" (= dtype) | "f16"
 
     @property
     def qkv_dim(self) -> int:
@@ -70,6 +72,11 @@ class Shape:
     @property
     def q_dim(self) -> int:
         return self.nq * self.head_dim
+
+    @property
+    def kv_dtype(self) -> str:
+        """Storage type of the KV caches."""
+        return "f16" if self.kv == "f16" else self.dtype
 
     def replace(self, **kw) -> "Shape":
         return dataclasses.replace(self, **kw)
@@ -135,6 +142,8 @@ def to_storage(x64: np.ndarray, dtype: str) -> np.ndarray:
         return x64.astype(np.float32)
     if dtype == "bf16":
         return f64_to_bf16_bits(x64)
+    if dtype == "f16":
+        return x64.astype(np.float16)      # nearest-even
     raise ValueError(dtype)
 
 
@@ -144,15 +153,19 @@ def widen(a: np.ndarray, dtype: str) -> np.ndarray:
         return np.asarray(a, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         return bf16_bits_to_f64(a)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.float16).astype(np.float64)
     raise ValueError(dtype)
 
 
 def sentinel(dtype: str):
+    if dtype == "f16":
+        return SENTINEL_F16.view(np.float16)
     return SENTINEL_F32 if dtype == "f32" else SENTINEL_BF16
 
 
 def storage_np_dtype(dtype: str):
-    return np.float32 if dtype == "f32" else np.uint16
+    return {"f32": np.float32, "bf16": np.uint16, "f16": np.float16}[dtype]
 
 
 # ---------------------------------------------------------------------------
@@ -230,12 +243,13 @@ def kv_caches(shape: Shape) -> tuple[np.ndarray, np.ndarray]:
     """
     L, nkv, S, hd, s = shape.n_layers, shape.nkv, shape.max_seq, shape.head_dim, shape.start
     rng = _rng(shape.seed * 1000 + 901)
+    kd = shape.kv_dtype
     out = []
     for _ in range(2):
-        c = np.full((L, nkv, S, hd), sentinel(shape.dtype), dtype=storage_np_dtype(shape.dtype))
+        c = np.full((L, nkv, S, hd), sentinel(kd), dtype=storage_np_dtype(kd))
         if s:
             vals = rng.standard_normal((L, nkv, s, hd))
-            c[:, :, :s, :] = to_storage(vals, shape.dtype).view(c.dtype)
+            c[:, :, :s, :] = to_storage(vals, kd).view(c.dtype)
         out.append(c)
     return out[0], out[1]
 

@@ -91,7 +91,7 @@ class GpuRun:
 
 
 def widen_caches(shape, kc, vc):
-    return synth.widen(kc, shape.dtype), synth.widen(vc, shape.dtype)
+    return synth.widen(kc, shape.kv_dtype), synth.widen(vc, shape.kv_dtype)
 
 
 def oracle_layer(shape, w_np, layer, x_np, kc_np, vc_np, rows=None):
@@ -110,10 +110,10 @@ def check_cache_slots(shape, layer, n, start, kc_in, kc_gpu):
     so every written slot must change (to finite values) and every other slot
     must keep its bits.
     """
-    u = np.uint16 if kc_in.dtype == np.uint16 else np.uint32
+    u = np.uint32 if kc_in.dtype == np.float32 else np.uint16
     slot_changed = (kc_gpu.view(u) != kc_in.view(u)).any(axis=-1)      # [L][nkv][max_seq]
     expect = np.zeros_like(slot_changed)
     expect[layer, :, start:start + n] = True
-    written = synth.widen(kc_gpu[layer, :, start:start + n], shape.dtype)
+    written = synth.widen(kc_gpu[layer, :, start:start + n], shape.kv_dtype)
     assert np.all(np.isfinite(written)), "a written cache slot holds non-finite values"
     assert np.array_equal(slot_changed, expect), "cache slots changed outside [start, start+n)"

@@ -445,3 +445,44 @@ def test_verify_tail_rows_are_normed_independently():
     scaled = x * np.array([[1.0], [7.0], [0.25]])
     got, _ = oracle.verify_tail(scaled, g, 0.0, W)
     np.testing.assert_allclose(got, base, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- fp16 KV cache
+
+@pytest.mark.parametrize("case", _golden()["f16_cache"])
+def test_f16_cache_rounding_hand_cases(case):
+    ns = dict(MATH_NS, inf=math.inf)
+    x = eval(case["x"], {"__builtins__": {}}, ns)
+    exp = eval(case["expected"], {"__builtins__": {}}, ns)
+    sh = synth.WORKLOADS["tiny-f32"].replace(dtype="bf16", kv="f16")
+    got = oracle.cache_store(sh, np.array([x, -x]))
+    assert got[0] == exp and got[1] == -exp
+
+
+def test_act_format_cache_is_exact():
+    sh = synth.WORKLOADS["tiny-f32"]
+    x = np.array([1 + 2.0 ** -40, math.pi])
+    assert np.array_equal(oracle.cache_store(sh, x), x)
+
+
+def test_layer_with_f16_cache_stores_rounded_keys_and_reads_them():
+    # the f16-cache layer equals the exact layer run on caches whose written
+    # slots are the halves of the exact ones: store rounding is the only change
+    sh = synth.WORKLOADS["tiny-f32"].replace(dtype="bf16", n_tokens=6, start=3, max_seq=16)
+    sh16 = sh.replace(kv="f16")
+    w = synth.widen_layer(sh, synth.layer_weights(sh, 0))
+    x = synth.widen(synth.hidden_input(sh), sh.dtype)
+    kc, vc = synth.kv_caches(sh16)
+    k16, v16 = synth.widen(kc, "f16"), synth.widen(vc, "f16")
+    out16 = oracle.prefill_layer(sh16, w, 0, x, sh.start, k16, v16)
+    pos = sh.start + np.arange(sh.n_tokens)
+    _, k, v = oracle.qkv_rows(sh, w, x, pos)
+    assert np.array_equal(k16[0][:, sh.start:sh.start + sh.n_tokens],
+                          k.transpose(1, 0, 2).astype(np.float16).astype(np.float64))
+    assert np.array_equal(v16[0][:, sh.start:sh.start + sh.n_tokens],
+                          v.transpose(1, 0, 2).astype(np.float16).astype(np.float64))
+    # the same layer with exact caches differs, but only by about the rounding
+    k64, v64 = synth.widen(kc, "f16"), synth.widen(vc, "f16")
+    out = oracle.prefill_layer(sh, w, 0, x, sh.start, k64, v64)
+    assert not np.array_equal(out, out16)
+    assert np.abs(out - out16).max() <= 1e-2 * np.abs(out).max()

@@ -50,8 +50,10 @@ def _check_layer(shape, rows=None, layer=0, label=""):
     errs = {
         "hidden": rel_err(g_hidden[sel], out),
         "delta": rel_err(g_res[sel] - x64[sel], out - x64[sel]),
-        "k_slots": rel_err(synth.widen(g_kc[layer, :, s:s + n], sh.dtype), kc64[layer, :, s:s + n]),
-        "v_slots": rel_err(synth.widen(g_vc[layer, :, s:s + n], sh.dtype), vc64[layer, :, s:s + n]),
+        "k_slots": rel_err(synth.widen(g_kc[layer, :, s:s + n], sh.kv_dtype),
+                           kc64[layer, :, s:s + n]),
+        "v_slots": rel_err(synth.widen(g_vc[layer, :, s:s + n], sh.kv_dtype),
+                           vc64[layer, :, s:s + n]),
     }
     log(f"[parity] {label or shape.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, v in errs.items():
@@ -122,6 +124,31 @@ DECODE = [
 @pytest.mark.parametrize("shape", DECODE, ids=[s.name for s in DECODE])
 def test_decode_layer(shape):
     _check_layer(shape)
+
+
+# fp16 KV cache (the pages' cache type): K and V rounded to IEEE half when
+# stored, attention on fp16 MFMAs
+KV16 = [
+    _small("kv16-g4-ragged", kv="f16"),
+    _small("kv16-g1-hd64-qknorm", hidden=384, inter=1024, nq=4, nkv=4, head_dim=64,
+           qk_norm=True, eps=1e-6, n_tokens=77, start=0, max_seq=128, kv="f16"),
+    _small("kv16-8wave-g4", hidden=256, inter=512, nq=32, nkv=8, head_dim=128,
+           n_tokens=1990, start=0, max_seq=2048, kv="f16"),
+    _small("kv16-decode-split", hidden=256, inter=512, nq=4, nkv=2, n_tokens=3, start=900,
+           max_seq=1024, kv="f16"),
+]
+
+
+@pytest.mark.parametrize("shape", KV16, ids=[s.name for s in KV16])
+def test_kv16_layer(shape):
+    _check_layer(shape)
+
+
+@pytest.mark.timeout(600)
+def test_kv16_llama3_sampled():
+    sh = synth.WORKLOADS["llama3-8b-layer"].replace(name="llama3-8b-layer-kv16", kv="f16",
+                                                     start=1000, max_seq=2048)
+    _check_layer(sh, rows=_sample_rows(sh.n_tokens, seed=3))
 
 
 @pytest.mark.timeout(600)
@@ -202,7 +229,7 @@ def test_chunk_matches_oracle_and_is_chunking_invariant():
         x64 = synth.widen(x, sh.dtype)
         e_d = rel_err(res - x64[last:], ref[last:] - x64[last:])
         e_l = rel_err(logits.cpu().numpy(), ref_logits)
-        e_k = rel_err(synth.widen(g_kc[:, :, sh.start:sh.start + sh.n_tokens], sh.dtype),
+        e_k = rel_err(synth.widen(g_kc[:, :, sh.start:sh.start + sh.n_tokens], sh.kv_dtype),
                       kc64[:, :, sh.start:sh.start + sh.n_tokens])
         log(f"[parity] chunk mb={mb}: hidden={e_h:.2e} delta={e_d:.2e} logits={e_l:.2e} "
             f"k={e_k:.2e}")
@@ -251,8 +278,8 @@ def test_stack32_chunked_prefill():
     # (a) layer 0 K/V for all tokens: steps 1-3 of the oracle on the input rows
     w0 = synth.widen_layer(sh, layers[0])
     q, k, v = oracle.qkv_rows(sh, w0, synth.widen(x, sh.dtype), np.arange(sh.n_tokens))
-    e_k = rel_err(synth.widen(g_k0, sh.dtype).transpose(1, 0, 2), k)
-    e_v = rel_err(synth.widen(g_v0, sh.dtype).transpose(1, 0, 2), v)
+    e_k = rel_err(synth.widen(g_k0, sh.kv_dtype).transpose(1, 0, 2), k)
+    e_v = rel_err(synth.widen(g_v0, sh.kv_dtype).transpose(1, 0, 2), v)
     # (b) head on the GPU's last row
     ref_logits = oracle.lm_head_logits(g[-1], synth.widen(fn, sh.dtype), sh.eps,
                                        synth.widen(W, sh.dtype))

@@ -6,7 +6,7 @@ supplies device memory and streams.  Build the library with
 """
 from ._lib import (EXPORTS, KERNELS, LIB_PATH, TLP_BF16, TLP_ERR_HIP, TLP_ERR_NULL,
                    TLP_ERR_POSITION, TLP_ERR_SHAPE, TLP_ERR_UNSUPPORTED, TLP_ERR_WORKSPACE,
-                   TLP_F32, TLP_OK, TLP_W_DENSE, TLP_W_SIGN1_G128, WS_ACT, WS_ATTN, WS_COUNT,
+                   TLP_F32, TLP_KV_ACT, TLP_KV_F16, TLP_OK, TLP_W_DENSE, TLP_W_SIGN1_G128, WS_ACT, WS_ATTN, WS_COUNT,
                    WS_HEAD, WS_PART, WS_QKV, WS_RES, WS_XN, Config, LayerWeights, TlpError,
                    Weight, argmax_rows, lib, make_config, prefill_chunk, prefill_layer,
                    profile_begin, profile_end, rope_table, verify_tail, verify_workspace_bytes,
@@ -17,5 +17,5 @@ __all__ = ["EXPORTS", "KERNELS", "LIB_PATH", "profile_begin", "profile_end", "Co
            "prefill_layer", "rope_table", "workspace_bytes", "workspace_layout", "argmax_rows",
            "verify_tail", "verify_workspace_bytes", "TLP_OK", "TLP_ERR_NULL", "TLP_ERR_SHAPE",
            "TLP_ERR_POSITION", "TLP_ERR_UNSUPPORTED", "TLP_ERR_WORKSPACE", "TLP_ERR_HIP",
-           "TLP_F32", "TLP_BF16", "TLP_W_DENSE", "TLP_W_SIGN1_G128", "WS_RES", "WS_XN", "WS_QKV",
+           "TLP_F32", "TLP_BF16", "TLP_KV_ACT", "TLP_KV_F16", "TLP_W_DENSE", "TLP_W_SIGN1_G128", "WS_RES", "WS_XN", "WS_QKV",
            "WS_ATTN", "WS_ACT", "WS_HEAD", "WS_PART", "WS_COUNT"]

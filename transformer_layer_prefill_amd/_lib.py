@@ -17,6 +17,7 @@ TLP_OK, TLP_ERR_NULL, TLP_ERR_SHAPE, TLP_ERR_POSITION = 0, 1, 2, 3
 TLP_ERR_UNSUPPORTED, TLP_ERR_WORKSPACE, TLP_ERR_HIP = 4, 5, 6
 TLP_F32, TLP_BF16 = 0, 1
 TLP_W_DENSE, TLP_W_SIGN1_G128 = 0, 1
+TLP_KV_ACT, TLP_KV_F16 = 0, 1
 WS_RES, WS_XN, WS_QKV, WS_ATTN, WS_ACT, WS_HEAD, WS_PART, WS_COUNT = range(8)
 
 EXPORTS = ("tlp_workspace_bytes", "tlp_workspace_layout", "tlp_rope_table",
@@ -40,7 +41,7 @@ class Config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("n_layers", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("qk_norm", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("wformat", ctypes.c_int32)]
+                ("wformat", ctypes.c_int32), ("kv_format", ctypes.c_int32)]
 
 
 class Weight(ctypes.Structure):
@@ -122,9 +123,9 @@ def _stream(stream) -> int | None:
 
 
 def make_config(hidden, intermediate, n_q_heads, n_kv_heads, head_dim, max_seq, n_layers,
-                rms_eps, qk_norm, dtype, wformat=TLP_W_DENSE) -> Config:
+                rms_eps, qk_norm, dtype, wformat=TLP_W_DENSE, kv_format=TLP_KV_ACT) -> Config:
     return Config(hidden, intermediate, n_q_heads, n_kv_heads, head_dim, max_seq, n_layers,
-                  rms_eps, int(bool(qk_norm)), dtype, wformat)
+                  rms_eps, int(bool(qk_norm)), dtype, wformat, kv_format)
 
 
 def workspace_bytes(cfg: Config, max_tokens: int) -> int:

@@ -46,6 +46,10 @@ tlp_status check_config(const tlp_config* c) {
     return fail(TLP_ERR_UNSUPPORTED, "wformat %d is not a tlp_wformat", c->wformat);
   if (c->wformat == TLP_W_SIGN1_G128 && c->dtype != TLP_BF16)
     return fail(TLP_ERR_UNSUPPORTED, "1-bit weights need dtype TLP_BF16");
+  if (c->kv_format != TLP_KV_ACT && c->kv_format != TLP_KV_F16)
+    return fail(TLP_ERR_UNSUPPORTED, "kv_format %d is not a tlp_kv_format", c->kv_format);
+  if (c->kv_format == TLP_KV_F16 && c->dtype != TLP_BF16)
+    return fail(TLP_ERR_UNSUPPORTED, "an fp16 KV cache needs dtype TLP_BF16");
   if (c->hidden <= 0 || c->intermediate <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
       c->max_seq <= 0 || c->n_layers <= 0)
     return fail(TLP_ERR_SHAPE, "sizes must be positive");
@@ -288,15 +292,16 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
     TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemm(g, s));
   }
   // 3a-3d. (slice sum,) QK-norm, RoPE, KV-cache store
+  const bool kv16 = c.kv_format == TLP_KV_F16;
   TLP_LAUNCH(TLP_K_QK_ROPE_KV,
-             launch_qk_rope_store(act, qkv, n, qkv_dim, part, q_parts, qkv_part_stride, w.q_norm,
-                                  w.k_norm, c.qk_norm != 0, c.rms_eps, cs, sn, k_layer, v_layer,
-                                  c.max_seq, start, nq, nkv, hd, s));
+             launch_qk_rope_store(act, kv16, qkv, n, qkv_dim, part, q_parts, qkv_part_stride,
+                                  w.q_norm, w.k_norm, c.qk_norm != 0, c.rms_eps, cs, sn, k_layer,
+                                  v_layer, c.max_seq, start, nq, nkv, hd, s));
   // 3e. causal GQA attention
   // (the PART region is free here: the QKV slices have been summed)
   TLP_LAUNCH(TLP_K_ATTENTION,
-             launch_attention(act, qkv, qkv_dim, k_layer, v_layer, attn, qd, n, start, nq, nkv,
-                              hd, c.max_seq, split ? part : nullptr, L.part_floats, s));
+             launch_attention(act, kv16, qkv, qkv_dim, k_layer, v_layer, attn, qd, n, start, nq,
+                              nkv, hd, c.max_seq, split ? part : nullptr, L.part_floats, s));
   // 4. output projection: split-K slices (bf16) or a fused residual add (fp32)
   int o_parts = 0;
   g = GemmCall{};

@@ -5,13 +5,16 @@
 // one query position at a time with a materialised score row; here it is one
 // flash-style kernel with an online softmax and no score buffer.
 //
-// bf16 kernel (gfx950 MFMA).  A block owns one kv head and a tile of query
+// bf16 kernel (gfx950 MFMA; with an fp16 cache the same kernel runs
+// v_mfma_f32_32x32x16_f16 on fp16 K, V, Q and P).  A block owns one kv head and a tile of query
 // tokens; its four or eight wavefronts are (query head of the group, 32-token
 // slice) pairs that share every K/V block staged in LDS, so K/V are read once
 // per group and tile.  Per 64-key block a wavefront computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (lane = query, 32 key scores per lane), runs the
 // online softmax in fp32 with exp2, and accumulates O^T = V^T P^T, taking P
 // straight from the score registers and V^T from transposing LDS reads.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -49,8 +52,30 @@ struct AttnArgs {
 // 4)) so the four rows x 64 bytes of a transposing step do.  Key rows past
 // the last visible key are clamped to it (finite data that the mask gives a
 // zero weight), so unwritten cache slots never reach the products.
-template <int HD, int NW, bool SPLIT>
+// MFMA operands of the bf16 cache, or of the fp16 cache (Q converted to fp16
+// when loaded, P rounded to fp16).
+template <bool KV16> struct AttnOps;
+template <> struct AttnOps<false> {
+  typedef bf16x8_t V8;
+  static __device__ __forceinline__ f32x16_t mma(V8 a, V8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ __bf16 cvt(float x) { return static_cast<__bf16>(x); }
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) { return dot2_bf16_sum(pair, acc); }
+};
+template <> struct AttnOps<true> {
+  typedef f16x8_t V8;
+  static __device__ __forceinline__ f32x16_t mma(V8 a, V8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ _Float16 cvt(float x) { return static_cast<_Float16>(x); }
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) { return dot2_f16_sum(pair, acc); }
+};
+
+template <int HD, int NW, bool SPLIT, bool KV16>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs a) {
+  typedef AttnOps<KV16> Ops;
+  typedef typename Ops::V8 V8;
   constexpr int KB = 64;                 // keys per block
   constexpr int ROWB = HD * 2;           // bytes per key row
   constexpr int CH = ROWB / 16;          // 16-byte chunks per row
@@ -95,7 +120,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   const int pos_lo = a.start + t0w;                   // every key <= pos_lo is visible to the wave
 
   // Q^T fragments (B operand): lane holds Q[t][ks*16 + lh*8 .. +8]
-  bf16x8_t qf[KS];
+  V8 qf[KS];
   {
     const uint16_t* qrow = a.q + static_cast<size_t>(q_ok ? t : 0) * a.q_ld + h * HD;
     const uint32_t keep = q_ok ? 0xffffffffu : 0u;
@@ -103,7 +128,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
     for (int ks = 0; ks < KS; ++ks) {
       uint4 u = *reinterpret_cast<const uint4*>(qrow + ks * 16 + lh * 8);
       u = make_uint4(u.x & keep, u.y & keep, u.z & keep, u.w & keep);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, u);
+      if constexpr (KV16) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          qf[ks][e] = static_cast<_Float16>(bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)))));
+      } else {
+        qf[ks] = __builtin_bit_cast(bf16x8_t, u);
+      }
     }
   }
 
@@ -162,9 +194,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
       const int krow = hb * 32 + lr;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+        const V8 kf = *reinterpret_cast<const V8*>(
             Kt + krow * ROWB + (((ks * 2 + lh) ^ swz_k(krow)) << 4));
-        sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[hb], 0, 0, 0);
+        sc[hb] = Ops::mma(kf, qf[ks], sc[hb]);
       }
     }
   };
@@ -252,21 +284,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
     scores(min(kb + 1, kb_hi - 1), s_next);
     // (a key range of the split form may hide every key from a row so far)
     const float neg_m = SPLIT && m_run == -INFINITY ? 0.f : -m_run;
-    bf16x8_t pf[4];   // B operand of step 2*hb + half: slots (lh, e) <- r = 8*half + e
+    V8 pf[4];   // B operand of step 2*hb + half: slots (lh, e) <- r = 8*half + e
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        pf[hb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(fast_exp2(fmaf(s[hb][r], c, neg_m)));
+        pf[hb * 2 + (r >> 3)][r & 7] = Ops::cvt(fast_exp2(fmaf(s[hb][r], c, neg_m)));
     // the row sum takes the same bf16 weights the products use, two per dot2
     float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 u = __builtin_bit_cast(uint4, pf[i]);
-      psum0 = dot2_bf16_sum(u.x, psum0);
-      psum1 = dot2_bf16_sum(u.y, psum1);
-      psum0 = dot2_bf16_sum(u.z, psum0);
-      psum1 = dot2_bf16_sum(u.w, psum1);
+      psum0 = Ops::sum2(u.x, psum0);
+      psum1 = Ops::sum2(u.y, psum1);
+      psum0 = Ops::sum2(u.z, psum0);
+      psum1 = Ops::sum2(u.w, psum1);
     }
     l_run += psum0 + psum1;
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // 4 K fragment reads ahead
@@ -292,8 +324,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
                                        (dim & 7) * 2);
         const uint2 hi = lds_read_tr16(Vt + r1 * ROWB + (((dim >> 3) ^ swz_v(r1)) << 4) +
                                        (dim & 7) * 2);
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], o[d], 0, 0, 0);
+        const V8 vf = __builtin_bit_cast(V8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[d] = Ops::mma(vf, pf[st], o[d]);
       }
     }
   };
@@ -450,7 +482,7 @@ size_t attention_split_floats(int M, int kv_len, int nq, int nkv, int head_dim) 
   return ns < 2 ? 0 : static_cast<size_t>(ns) * M * nq * (head_dim + 2);
 }
 
-hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_layer,
+hipError_t launch_attention(Act act, bool kv16, const void* q, int q_ld, const void* k_layer,
                             const void* v_layer, void* out, int out_ld, int M, int start,
                             int nq, int nkv, int head_dim, int max_seq, float* split_ws,
                             size_t split_ws_floats, hipStream_t s) {
@@ -490,8 +522,13 @@ hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_laye
     a.po = split_ws;
     a.pml = split_ws + static_cast<size_t>(ns) * M * nq * head_dim;
     dim3 grid(gr.blocks * ns);
-    if (head_dim == 128) attn_fwd_bf16_kernel<128, 4, true><<<grid, 256, 0, s>>>(a);
-    else attn_fwd_bf16_kernel<64, 4, true><<<grid, 256, 0, s>>>(a);
+    if (kv16) {
+      if (head_dim == 128) attn_fwd_bf16_kernel<128, 4, true, true><<<grid, 256, 0, s>>>(a);
+      else attn_fwd_bf16_kernel<64, 4, true, true><<<grid, 256, 0, s>>>(a);
+    } else {
+      if (head_dim == 128) attn_fwd_bf16_kernel<128, 4, true, false><<<grid, 256, 0, s>>>(a);
+      else attn_fwd_bf16_kernel<64, 4, true, false><<<grid, 256, 0, s>>>(a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 cgrid(M, nq);
@@ -502,13 +539,15 @@ hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_laye
     return hipGetLastError();
   }
   dim3 grid(gr.blocks);
+#define TLP_ATTN(HD_, KV_)                                                                  \
+  if (a.waves == 8) attn_fwd_bf16_kernel<HD_, 8, false, KV_><<<grid, 512, 0, s>>>(a);       \
+  else attn_fwd_bf16_kernel<HD_, 4, false, KV_><<<grid, 256, 0, s>>>(a);
   if (head_dim == 128) {
-    if (a.waves == 8) attn_fwd_bf16_kernel<128, 8, false><<<grid, 512, 0, s>>>(a);
-    else attn_fwd_bf16_kernel<128, 4, false><<<grid, 256, 0, s>>>(a);
+    if (kv16) { TLP_ATTN(128, true) } else { TLP_ATTN(128, false) }
   } else {
-    if (a.waves == 8) attn_fwd_bf16_kernel<64, 8, false><<<grid, 512, 0, s>>>(a);
-    else attn_fwd_bf16_kernel<64, 4, false><<<grid, 256, 0, s>>>(a);
+    if (kv16) { TLP_ATTN(64, true) } else { TLP_ATTN(64, false) }
   }
+#undef TLP_ATTN
   return hipGetLastError();
 }
 

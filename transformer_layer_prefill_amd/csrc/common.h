@@ -37,6 +37,14 @@ template <> struct Elt<uint16_t> {
   static __device__ __forceinline__ uint16_t st(float v) { return f32_to_bf16(v); }
 };
 
+// IEEE fp16 storage (KV-cache format); stores round to nearest-even.
+typedef _Float16 f16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+template <> struct Elt<f16_t> {
+  static __device__ __forceinline__ float ld(f16_t v) { return static_cast<float>(v); }
+  static __device__ __forceinline__ f16_t st(float v) { return static_cast<f16_t>(v); }
+};
+
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return Elt<T>::ld(v); }
 template <typename T> __device__ __forceinline__ T from_f32(float v) { return Elt<T>::st(v); }
 
@@ -67,6 +75,13 @@ __device__ __forceinline__ float block_sum(float v, float* red /* LDS, NW floats
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// acc + lo + hi for a pair of fp16 values packed in one word
+__device__ __forceinline__ float dot2_f16_sum(uint32_t pair, float acc) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pair),
+                                __builtin_bit_cast(f16x2_t, 0x3C003C00u), acc, false);
+}
 
 // acc + lo + hi for a pair of bf16 values packed in one word (v_dot2 with 1.0)
 __device__ __forceinline__ float dot2_bf16_sum(uint32_t pair, float acc) {

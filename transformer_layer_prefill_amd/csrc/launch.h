@@ -81,7 +81,8 @@ hipError_t launch_swiglu_finish(const float* part, int splits, size_t part_strid
 // (raw) into cache slot start + t of every kv head of this layer.  The input row
 // is qkv itself (n_part == 0) or the sum of n_part fp32 split-K slices of
 // row stride qkv_ld, part_stride elements apart.
-hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const float* part,
+// kv16: the caches hold IEEE fp16 (bf16 activations only).
+hipError_t launch_qk_rope_store(Act act, bool kv16, void* qkv, int M, int qkv_ld, const float* part,
                                 int n_part, size_t part_stride, const void* q_gain,
                                 const void* k_gain, bool qk_norm, float eps,
                                 const float* rope_cos, const float* rope_sin, void* k_layer,
@@ -98,7 +99,7 @@ hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const flo
 constexpr int kAttnMaxSplits = 64;
 int attention_kv_splits(int M, int kv_len, int nq, int nkv);
 size_t attention_split_floats(int M, int kv_len, int nq, int nkv, int head_dim);
-hipError_t launch_attention(Act act, const void* q, int q_ld, const void* k_layer,
+hipError_t launch_attention(Act act, bool kv16, const void* q, int q_ld, const void* k_layer,
                             const void* v_layer, void* out, int out_ld, int M, int start,
                             int nq, int nkv, int head_dim, int max_seq, float* split_ws,
                             size_t split_ws_floats, hipStream_t s);

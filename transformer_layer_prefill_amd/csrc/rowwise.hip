@@ -122,12 +122,12 @@ hipError_t launch_rownorm(Act act, const RowArgs& a, hipStream_t s) {
 // The projected row is either qkv itself (activation type) or, when the QKV
 // GEMM split K, the sum of its n_part fp32 slices; roped Q is written back into
 // qkv for the attention kernel either way.
-template <typename T>
+template <typename T, typename C>
 __global__ __launch_bounds__(256) void qk_rope_store_kernel(
     T* __restrict__ qkv, int qkv_ld, const float* __restrict__ part, int n_part,
     size_t part_stride, const T* __restrict__ q_gain, const T* __restrict__ k_gain,
     int qk_norm, float eps, const float* __restrict__ rope_cos,
-    const float* __restrict__ rope_sin, T* __restrict__ k_layer, T* __restrict__ v_layer,
+    const float* __restrict__ rope_sin, C* __restrict__ k_layer, C* __restrict__ v_layer,
     int max_seq, int start, int nq, int nkv, int hd) {
   const int t = blockIdx.x;
   const int pos = start + t;
@@ -150,8 +150,8 @@ __global__ __launch_bounds__(256) void qk_rope_store_kernel(
   for (int hh = blockIdx.y * 4 + wave; hh < n_heads; hh += gridDim.y * 4) {
     if (hh >= nq + nkv) {  // V head: raw copy into the cache slot
       const int j = hh - nq - nkv;
-      T* dst = v_layer + (static_cast<size_t>(j) * max_seq + pos) * hd;
-      for (int i = lane; i < hd; i += 64) dst[i] = from_f32<T>(in(hh * hd + i));
+      C* dst = v_layer + (static_cast<size_t>(j) * max_seq + pos) * hd;
+      for (int i = lane; i < hd; i += 64) dst[i] = from_f32<C>(in(hh * hd + i));
       continue;
     }
     const bool active = lane < half;
@@ -174,14 +174,18 @@ __global__ __launch_bounds__(256) void qk_rope_store_kernel(
     const float sn = rope_sin[static_cast<size_t>(pos) * half + lane];
     const float y1 = x1 * c - x2 * sn;
     const float y2 = x2 * c + x1 * sn;
-    T* dst = hh < nq ? row + hh * hd
-                     : k_layer + (static_cast<size_t>(hh - nq) * max_seq + pos) * hd;
-    dst[lane] = from_f32<T>(y1);
-    dst[lane + half] = from_f32<T>(y2);
+    if (hh < nq) {
+      row[hh * hd + lane] = from_f32<T>(y1);
+      row[hh * hd + lane + half] = from_f32<T>(y2);
+    } else {
+      C* dst = k_layer + (static_cast<size_t>(hh - nq) * max_seq + pos) * hd;
+      dst[lane] = from_f32<C>(y1);
+      dst[lane + half] = from_f32<C>(y2);
+    }
   }
 }
 
-hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const float* part,
+hipError_t launch_qk_rope_store(Act act, bool kv16, void* qkv, int M, int qkv_ld, const float* part,
                                 int n_part, size_t part_stride, const void* q_gain,
                                 const void* k_gain, bool qk_norm, float eps,
                                 const float* rope_cos, const float* rope_sin, void* k_layer,
@@ -191,13 +195,19 @@ hipError_t launch_qk_rope_store(Act act, void* qkv, int M, int qkv_ld, const flo
   if (n_part > 8) return hipErrorInvalidValue;
   dim3 grid(M, (nq + 2 * nkv + 3) / 4), block(256);
   if (act == Act::F32)
-    qk_rope_store_kernel<float><<<grid, block, 0, s>>>(
+    qk_rope_store_kernel<float, float><<<grid, block, 0, s>>>(
         static_cast<float*>(qkv), qkv_ld, part, n_part, part_stride,
         static_cast<const float*>(q_gain), static_cast<const float*>(k_gain), qk_norm ? 1 : 0,
         eps, rope_cos, rope_sin, static_cast<float*>(k_layer), static_cast<float*>(v_layer),
         max_seq, start, nq, nkv, head_dim);
+  else if (kv16)
+    qk_rope_store_kernel<uint16_t, f16_t><<<grid, block, 0, s>>>(
+        static_cast<uint16_t*>(qkv), qkv_ld, part, n_part, part_stride,
+        static_cast<const uint16_t*>(q_gain), static_cast<const uint16_t*>(k_gain),
+        qk_norm ? 1 : 0, eps, rope_cos, rope_sin, static_cast<f16_t*>(k_layer),
+        static_cast<f16_t*>(v_layer), max_seq, start, nq, nkv, head_dim);
   else
-    qk_rope_store_kernel<uint16_t><<<grid, block, 0, s>>>(
+    qk_rope_store_kernel<uint16_t, uint16_t><<<grid, block, 0, s>>>(
         static_cast<uint16_t*>(qkv), qkv_ld, part, n_part, part_stride,
         static_cast<const uint16_t*>(q_gain), static_cast<const uint16_t*>(k_gain),
         qk_norm ? 1 : 0, eps, rope_cos, rope_sin, static_cast<uint16_t*>(k_layer),

@@ -44,7 +44,9 @@ def config_of(shape) -> _lib.Config:
                             shape.max_seq, shape.n_layers, shape.eps, shape.qk_norm,
                             _lib.TLP_F32 if shape.dtype == "f32" else _lib.TLP_BF16,
                             _lib.TLP_W_SIGN1_G128 if shape.wformat == "sign1"
-                            else _lib.TLP_W_DENSE)
+                            else _lib.TLP_W_DENSE,
+                            _lib.TLP_KV_F16 if getattr(shape, "kv", "act") == "f16"
+                            else _lib.TLP_KV_ACT)
 
 
 class DeviceLayer:
