@@ -40,16 +40,19 @@ __device__ __forceinline__ void store8(float* p, const float v[8]) {
   reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// One 256-thread block per row.  The row is assembled once in registers:
+// One block of NT threads per row.  The row is assembled once in registers:
 // x (activation type or fp32) plus the split-K partial sums of the projection
 // that produced it; the sum may be stored as the fp32 residual stream and/or
 // rounded to the activation type, and RMSNorm(sum) * gain is written when a
-// gain is given.  Up to 8 chunks of 8 elements per thread (H <= 16384).
-template <typename T, bool XF32, bool NORM_F32>
-__global__ __launch_bounds__(256) void rownorm_kernel(RowArgs a) {
-  constexpr int CH = 8;       // chunks of 8 elements per thread (H <= 16384)
-  constexpr int MAXP = 8;     // partial slices summed per row
-  __shared__ float red[4];
+// gain is given.  NT is picked so that a thread holds one 8-element chunk
+// (two at H = 16384): the stores of one chunk may alias the loads of the next
+// (the residual is read and rewritten in place), so a second chunk per thread
+// would wait for a second round trip to memory.
+template <typename T, bool XF32, bool NORM_F32, int NT>
+__global__ __launch_bounds__(NT) void rownorm_kernel(RowArgs a) {
+  constexpr int CH = 2048 / NT;   // chunks of 8 elements per thread (H <= 16384)
+  constexpr int MAXP = 8;         // partial slices summed per row
+  __shared__ float red[NT / 64];
   const int r = blockIdx.x;
   const int chunks = a.H >> 3;
   const size_t roff = static_cast<size_t>(r) * a.H;
@@ -57,7 +60,7 @@ __global__ __launch_bounds__(256) void rownorm_kernel(RowArgs a) {
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int idx = threadIdx.x + c * 256;
+    const int idx = threadIdx.x + c * NT;
     if (idx >= chunks) break;
     // issue the row chunk and every partial slice before summing
     if constexpr (XF32)
@@ -80,11 +83,11 @@ __global__ __launch_bounds__(256) void rownorm_kernel(RowArgs a) {
       store8(static_cast<T*>(a.act_out) + static_cast<size_t>(r) * a.ld_act + idx * 8, v[c]);
   }
   if (!a.gain) return;
-  ss = block_sum<4>(ss, red);
+  ss = block_sum<NT / 64>(ss, red);
   const float inv = rsqrtf(ss / static_cast<float>(a.H) + a.eps);
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int idx = threadIdx.x + c * 256;
+    const int idx = threadIdx.x + c * NT;
     if (idx >= chunks) break;
     float g[8];
     load8(static_cast<const T*>(a.gain) + idx * 8, g);
@@ -97,17 +100,25 @@ __global__ __launch_bounds__(256) void rownorm_kernel(RowArgs a) {
   }
 }
 
-template <typename T>
-static hipError_t rownorm_t(const RowArgs& a, hipStream_t s) {
-  dim3 grid(a.rows), block(256);
+template <typename T, int NT>
+static hipError_t rownorm_nt(const RowArgs& a, hipStream_t s) {
+  dim3 grid(a.rows), block(NT);
   if (a.x_f32) {
-    if (a.norm_f32) rownorm_kernel<T, true, true><<<grid, block, 0, s>>>(a);
-    else rownorm_kernel<T, true, false><<<grid, block, 0, s>>>(a);
+    if (a.norm_f32) rownorm_kernel<T, true, true, NT><<<grid, block, 0, s>>>(a);
+    else rownorm_kernel<T, true, false, NT><<<grid, block, 0, s>>>(a);
   } else {
-    if (a.norm_f32) rownorm_kernel<T, false, true><<<grid, block, 0, s>>>(a);
-    else rownorm_kernel<T, false, false><<<grid, block, 0, s>>>(a);
+    if (a.norm_f32) rownorm_kernel<T, false, true, NT><<<grid, block, 0, s>>>(a);
+    else rownorm_kernel<T, false, false, NT><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t rownorm_t(const RowArgs& a, hipStream_t s) {
+  const int chunks = a.H >> 3;
+  if (chunks <= 256) return rownorm_nt<T, 256>(a, s);
+  if (chunks <= 512) return rownorm_nt<T, 512>(a, s);
+  return rownorm_nt<T, 1024>(a, s);
 }
 
 hipError_t launch_rownorm(Act act, const RowArgs& a, hipStream_t s) {
