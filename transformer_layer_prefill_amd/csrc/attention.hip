@@ -374,23 +374,47 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
 
 // Merge of the split-KV partial results of one (query row, head): with M the
 // largest running max, o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// The splits are spread over the block: threads take splits for the max and
+// the weights, then (head dim, split group) pairs for the weighted sum, so
+// the loads of different splits are in flight together.
 template <int HD>
-__global__ __launch_bounds__(HD) void attn_combine_kernel(const float* __restrict__ po,
-                                                         const float* __restrict__ pml,
-                                                         int n_split, int M, int nq,
-                                                         uint16_t* __restrict__ out, int out_ld) {
-  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-  float m = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp)
-    m = fmaxf(m, pml[((static_cast<size_t>(sp) * M + t) * nq + h) * 2]);
-  float l = 0.f, acc = 0.f;
-  for (int sp = 0; sp < n_split; ++sp) {
-    const size_t pr = (static_cast<size_t>(sp) * M + t) * nq + h;
-    const float wgt = fast_exp2(pml[pr * 2] - m);
-    l += pml[pr * 2 + 1] * wgt;
-    acc += po[pr * HD + d] * wgt;
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ po,
+                                                          const float* __restrict__ pml,
+                                                          int n_split, int M, int nq,
+                                                          uint16_t* __restrict__ out, int out_ld) {
+  constexpr int G = 256 / HD;   // split groups of the weighted sum
+  __shared__ float wgt[kAttnMaxSplits];
+  __shared__ float red[4];
+  __shared__ float acc_g[256];
+  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const size_t row = static_cast<size_t>(t) * nq + h;         // within one split
+  const size_t sstride = static_cast<size_t>(M) * nq;         // between splits
+  float mv = -INFINITY;
+  for (int sp = tid; sp < n_split; sp += 256) mv = fmaxf(mv, pml[(sp * sstride + row) * 2]);
+  mv = wave_max(mv);
+  if ((tid & 63) == 0) red[tid >> 6] = mv;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float lv = 0.f;
+  for (int sp = tid; sp < n_split; sp += 256) {
+    const float w = fast_exp2(pml[(sp * sstride + row) * 2] - m);
+    wgt[sp] = w;
+    lv += pml[(sp * sstride + row) * 2 + 1] * w;
   }
-  out[static_cast<size_t>(t) * out_ld + h * HD + d] = f32_to_bf16(acc / l);
+  const float l = block_sum<4>(lv, red);   // its barriers also publish wgt[]
+  const int d = tid % HD, grp = tid / HD;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int sp = grp; sp < n_split; sp += G) acc += po[(sp * sstride + row) * HD + d] * wgt[sp];
+  acc_g[tid] = acc;
+  __syncthreads();
+  if (tid < HD) {
+    float o = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < G; ++g2) o += acc_g[g2 * HD + tid];
+    out[static_cast<size_t>(t) * out_ld + h * HD + tid] = f32_to_bf16(o / l);
+  }
 }
 
 // fp32 kernel: one block per (query token, query head); keys in chunks of
@@ -533,9 +557,9 @@ hipError_t launch_attention(Act act, bool kv16, const void* q, int q_ld, const v
     if (e != hipSuccess) return e;
     dim3 cgrid(M, nq);
     if (head_dim == 128)
-      attn_combine_kernel<128><<<cgrid, 128, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+      attn_combine_kernel<128><<<cgrid, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
     else
-      attn_combine_kernel<64><<<cgrid, 64, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+      attn_combine_kernel<64><<<cgrid, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
     return hipGetLastError();
   }
   dim3 grid(gr.blocks);

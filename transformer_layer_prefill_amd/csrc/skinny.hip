@@ -36,7 +36,7 @@ __device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) {
 __device__ __forceinline__ bf16x8_t zero16() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
 
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
-  constexpr int STEPS = 16;   // 16-wide k-steps per main-loop iteration (256 of K)
+  constexpr int STEPS = 8;   // 16-wide k-steps per buffer (128 of K)
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= g.groups * g.splits) return;   // whole wavefronts
@@ -53,16 +53,35 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-  int k = k_begin;
-  for (; k + 16 * STEPS <= k_end; k += 16 * STEPS) {
-    bf16x8_t wv[STEPS], av[STEPS];
+  // Two register buffers of STEPS k-steps: the loads of the next 128 of K are
+  // issued before the MFMAs of the current ones.
+  bf16x8_t w0[STEPS], a0[STEPS], w1[STEPS], a1[STEPS];
+  auto load = [&](bf16x8_t (&wv)[STEPS], bf16x8_t (&av)[STEPS], int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < STEPS; ++j) wv[j] = ld16(wrow + k + 16 * j);
 #pragma unroll
     for (int j = 0; j < STEPS; ++j) av[j] = a_ok ? ld16(arow + k + 16 * j) : zero16();
+  };
+  auto mma = [&](const bf16x8_t (&wv)[STEPS], const bf16x8_t (&av)[STEPS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < STEPS; ++j)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[j], av[j], acc, 0, 0, 0);
+  };
+  constexpr int KB = 16 * STEPS;
+  int k = k_begin;
+  if (k + KB <= k_end) {
+    load(w0, a0, k);
+    k += KB;
+    for (;;) {
+      if (k + KB > k_end) { mma(w0, a0); break; }
+      load(w1, a1, k);
+      k += KB;
+      mma(w0, a0);
+      if (k + KB > k_end) { mma(w1, a1); break; }
+      load(w0, a0, k);
+      k += KB;
+      mma(w1, a1);
+    }
   }
   for (; k + 64 <= k_end; k += 64) {
     bf16x8_t wv[4], av[4];
