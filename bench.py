@@ -196,6 +196,88 @@ def bench_verify_tail(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_stack(args):
+    """The 32-layer chunked prefill: 4096 prompt tokens in micro-batches of
+    512 through 32 Llama-3-8B-shape layers, then the final norm and the
+    128256-row LM head on the last token.  One step is one tlp_prefill_chunk
+    call; value = 4096 * 32 / step time (tokens/s per layer)."""
+    import torch
+    import transformer_layer_prefill_amd as tlp
+    from transformer_layer_prefill_amd import tensors
+    sh = synth.WORKLOADS["llama3-8b-stack32"]
+    if args.kv_f16:
+        sh = sh.replace(kv="f16")
+    log(f"[bench] generating {sh.n_layers} layers and the head")
+    layers = synth.stack_weights(sh, workers=16)
+    dev = torch.device("cuda", 0)
+    dls = [tensors.DeviceLayer(w, dev) for w in layers]
+    del layers
+    x0 = tensors.to_device(synth.hidden_input(sh), dev)
+    kc, vc = synth.kv_caches(sh)
+    kcd, vcd = tensors.to_device(kc, dev), tensors.to_device(vc, dev)
+    del kc, vc
+    fn = tensors.to_device(synth.final_norm(sh), dev)
+    W = tensors.to_device(synth.lm_head(sh, workers=16), dev)
+    cfg = tensors.config_of(sh)
+    cos, sin = tlp.rope_table(sh.theta, sh.head_dim, sh.max_seq)
+    cosd, sind = tensors.to_device(cos, dev), tensors.to_device(sin, dev)
+    mb = sh.micro_batch
+    ws = torch.empty(tlp.workspace_bytes(cfg, min(sh.n_tokens, mb)), dtype=torch.uint8, device=dev)
+    logits = torch.empty(sh.vocab, dtype=torch.float32, device=dev)
+    structs = [d.struct for d in dls]
+    n_buf = args.warmup + 2 * args.steps
+    hiddens = [x0.clone() for _ in range(n_buf)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        tlp.prefill_chunk(cfg, structs, hiddens[i], sh.n_tokens, sh.start, mb, kcd, vcd, cosd,
+                          sind, ws, final_norm=fn, lm_head=W, vocab=sh.vocab, final_eps=sh.eps,
+                          logits=logits, stream=stream)
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    tlp.profile_begin()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    prof = tlp.profile_end()
+    kernels = {k: {"launches": n, "avg_us": round(1e3 * t / n, 3)} for k, (n, t) in prof.items() if n}
+    gemm_flops, _ = layer_flops(sh, mb, 0)
+    for k, f in gemm_flops.items():
+        kernels[k]["tflops"] = round(f / (kernels[k]["avg_us"] * 1e-6) / 1e12, 2)
+    dom_us = kernels["gate_up_gemm"]["avg_us"]
+    achieved = gemm_flops["gate_up_gemm"] / (dom_us * 1e-6) / 1e12
+    tokens_layers = sh.n_tokens * sh.n_layers
+    out = {
+        "metric": "prefill tokens/sec per layer, 32-layer chunked prefill + head",
+        "value": round(tokens_layers / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": sh.dtype,
+        "data": "synthetic",
+        "config": {"workload": sh.name, "tokens": sh.n_tokens, "layers": sh.n_layers,
+                   "micro_batch": mb, "vocab": sh.vocab, "kv_cache": sh.kv_dtype,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "gate_up_gemm", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_us": dom_us, "flops_per_launch": gemm_flops["gate_up_gemm"]},
+        "cpu_baseline": None,
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,7 +286,7 @@ def main():
     ap.add_argument("--workload", default="llama3-8b-layer",
                     choices=["llama3-8b-layer", "qwen3-8b-sign1-layer", "llama3-8b-long-ctx",
                              "llama3-8b-decode", "llama3-8b-long-decode",
-                             "llama3-8b-verify-tail"])
+                             "llama3-8b-verify-tail", "llama3-8b-stack32", "tiny-f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-f16", action="store_true",
                     help="keep the KV cache in IEEE fp16 (the pages' cache type)")
@@ -223,6 +305,9 @@ def main():
 
     if args.workload == "llama3-8b-verify-tail":
         bench_verify_tail(args)
+        return
+    if args.workload == "llama3-8b-stack32":
+        bench_stack(args)
         return
 
     import torch
@@ -338,7 +423,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": sh.dtype,
         "data": "synthetic",
         "config": {"workload": sh.name, "tokens": sh.n_tokens, "start_position": sh.start,
                    "hidden": sh.hidden, "intermediate": sh.inter, "q_heads": sh.nq,

@@ -431,6 +431,151 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
   gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh, split);
 }
 
+// ---- gate/up + SwiGLU with 112-column output tiles -----------------------------
+// A block covers 256 token rows and 112 output columns, i.e. 224 weight rows:
+// each of the two wavefront columns holds 56 gate and 56 up rows interleaved
+// eight by eight.  A 512-token micro-batch of an I = 14336 FFN then makes
+// 2 x 128 = 256 blocks, one per CU, where 256x256 tiles make 224 and leave 32
+// CUs idle.  Eight wavefronts of 64 rows x 112 weight rows use
+// v_mfma_f32_16x16x32_bf16 (4 x 7 fragments of 16x16); K tiles of 64 are
+// copied global -> LDS with global_load_lds_dwordx4 into a double buffer and
+// read with the same row swizzle as the 256x256 kernel.  In the 16x16 result
+// layout lane l holds column l % 16 of its fragment, so the gate value of an
+// output column sits eight lanes away from its up value.
+__device__ __forceinline__ void swiglu112_b_row(const GemmArgs& g, int nt, int rr, int& w_row) {
+  const int wn = rr / 112, q = rr % 112;
+  const int idx = min(nt * 112 + wn * 56 + 8 * (q / 16) + (q & 7), g.N - 1);
+  w_row = (q & 8) ? g.up_row + idx : idx;
+}
+
+__global__ __launch_bounds__(512) void gemm_swiglu112_kernel(GemmArgs g) {
+  constexpr int BM = 256, BR = 224, BK = 64, ROWB = 128;
+  constexpr int FM = 4, FN = 7;                             // 16x16 fragments per wavefront
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BR * ROWB;   // 32 KB + 28 KB
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_PW = 4, B_PW = 4;                         // DMA blocks per wavefront
+  constexpr int B_BLK = B_BYTES / 1024;                     // 28: wavefront 7 copies no B
+  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int wi = xcd_tile(blockIdx.x, gridDim.x);
+  const int mt = wi % g.m_tiles, nt = wi / g.m_tiles;
+  const int m0 = mt * BM;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l16 = lane & 15, lq = lane >> 4;
+
+  const int drow = lane >> 3, dslot = lane & 7;
+  const uint16_t* W = static_cast<const uint16_t*>(g.W);
+  const uint16_t* a_src[A_PW];
+  const uint16_t* b_src[B_PW];
+#pragma unroll
+  for (int j = 0; j < A_PW; ++j) {
+    const int row = (wave * A_PW + j) * 8 + drow;
+    a_src[j] = g.A + static_cast<size_t>(min(m0 + row, g.M - 1)) * g.lda + (dslot ^ swz8(row)) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < B_PW; ++j) {
+    const int rr = min((wave * B_PW + j) * 8 + drow, BR - 1);
+    int w_row;
+    swiglu112_b_row(g, nt, rr, w_row);
+    b_src[j] = W + static_cast<size_t>(w_row) * g.K + (dslot ^ swz8(rr)) * 8;
+  }
+  const bool has_b = wave * B_PW < B_BLK;   // wavefront-uniform
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * BK;
+    char* st = smem + (kt & 1) * STAGE;
+#pragma unroll
+    for (int j = 0; j < A_PW; ++j) dma16(a_src[j] + k0, st + (wave * A_PW + j) * 1024);
+    if (has_b) {
+#pragma unroll
+      for (int j = 0; j < B_PW; ++j)
+        dma16(b_src[j] + k0, st + A_BYTES + (wave * B_PW + j) * 1024);
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment rows are 16-aligned, so every row this lane reads has swz8(l16)
+  const int sw = swz8(l16);
+  const int a_off = (wm * 64 + l16) * ROWB, b_off = A_BYTES + (wn * 112 + l16) * ROWB;
+  const int ch0 = ((0 * 4 + lq) ^ sw) << 4, ch1 = ((1 * 4 + lq) ^ sw) << 4;
+  bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
+#define TLP_FRAGS16(AF, BF, ST, C)                                                           \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                     \
+      *reinterpret_cast<const bf16x8_t*>((ST) + a_off + i * 16 * ROWB + (C));                \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) BF[j] =                                     \
+      *reinterpret_cast<const bf16x8_t*>((ST) + b_off + j * 16 * ROWB + (C));
+#define TLP_MMA16(AF, BF)                                                                    \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i)                                             \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[i], BF[j], acc[i][j], 0, 0, 0);
+
+  // per 64-wide tile: two 32-wide k-steps; fragments of step 1 are read
+  // during the MFMAs of step 0, and the barrier + refill of the stage sit
+  // between the two MFMA groups
+  const int nk = g.K / BK;
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 1) {
+    if (has_b) __builtin_amdgcn_s_waitcnt(VmWait<A_PW + B_PW>::imm);
+    else __builtin_amdgcn_s_waitcnt(VmWait<A_PW>::imm);
+  } else {
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+  }
+  lds_barrier();
+  TLP_FRAGS16(af0, bf0, smem, ch0)
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+
+  int kt = 0;
+  for (; kt + 1 < nk; ++kt) {
+    const char* st = smem + (kt & 1) * STAGE;
+    TLP_FRAGS16(af1, bf1, st, ch1)
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA16(af0, bf0)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // tile kt+1, the only copy in flight
+    lds_barrier();
+    if (kt + 2 < nk) issue(kt + 2);
+    const char* st1 = smem + ((kt + 1) & 1) * STAGE;
+    TLP_FRAGS16(af0, bf0, st1, ch0)
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA16(af1, bf1)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    const char* st = smem + (kt & 1) * STAGE;
+    TLP_FRAGS16(af1, bf1, st, ch1)
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA16(af0, bf0)
+    TLP_MMA16(af1, bf1)
+  }
+#undef TLP_FRAGS16
+#undef TLP_MMA16
+
+  // epilogue: lane l holds column l16 of each fragment and rows 4*lq + r;
+  // columns 0-7 are gate, 8-15 the up values of the same output columns
+  uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = acc[i][j][r];
+        const float up = __shfl_xor(v, 8, 64);
+        const int m = m0 + wm * 64 + i * 16 + 4 * lq + r;
+        const int idx = nt * 112 + wn * 56 + 8 * j + l16;
+        if (l16 < 8 && m < g.M && idx < g.N)
+          out[static_cast<size_t>(m) * g.ldo + idx] = f32_to_bf16(silu_f32(v) * up);
+      }
+}
+
 // ---- fp32 FMA kernel --------------------------------------------------------
 // 64x64 tile, 256 threads; thread (tx, ty) owns rows ty*4..+4 and columns
 // {2tx, 2tx+1, 32+2tx, 33+2tx}, so the SwiGLU epilogue finds gate column c
@@ -551,8 +696,29 @@ int gemm_partial_splits(int M, int N, int K) {
   return splits < 1 ? 1 : splits;
 }
 
+// SwiGLU with dense weights and K % 64 == 0: 112-column tiles when they fill
+// whole waves of 256 blocks better than 128-column (256x256) tiles do.  Work
+// per block is 7/8 of a 256x256 tile, so compare waves x work.
+static bool use_swiglu112(const GemmArgs& g) {
+  if (g.K % 64) return false;
+  const long mt = (g.M + 255) / 256;
+  const long t128 = mt * ((g.N + 127) / 128), t112 = mt * ((g.N + 111) / 112);
+  const long w128 = (t128 + kCUs - 1) / kCUs, w112 = (t112 + kCUs - 1) / kCUs;
+  return w112 * 7 < w128 * 8;
+}
+
+static hipError_t run_swiglu112(GemmArgs g, hipStream_t s) {
+  g.m_tiles = (g.M + 255) / 256;
+  g.n_tiles = (g.N + 111) / 112;
+  g.splits = 1;
+  g.k_split = g.K;
+  gemm_swiglu112_kernel<<<g.m_tiles * g.n_tiles, 512, 0, s>>>(g);
+  return hipGetLastError();
+}
+
 template <int EPI, bool SIGN1, bool OUT_F32>
 static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
+  if (EPI == 2 && !SIGN1 && !OUT_F32 && use_swiglu112(g)) return run_swiglu112(g, s);
   const int cols_big = EPI == 2 ? 128 : 256;
   const long tiles_big = static_cast<long>((g.M + 255) / 256) * ((g.N + cols_big - 1) / cols_big);
   if (EPI == 4) {
