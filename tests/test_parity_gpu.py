@@ -160,6 +160,15 @@ def test_decode_llama3(n, start):
 
 
 @pytest.mark.timeout(600)
+def test_llama3_prefix_split_kv():
+    # a 512-token micro-batch after a 1536-slot prefix: 128 (tile, head) blocks
+    # take split key ranges, merged by one wavefront per (row, head)
+    sh = synth.WORKLOADS["llama3-8b-layer"].replace(name="llama3-8b-512@1536", start=1536,
+                                                     max_seq=2048)
+    _check_layer(sh, rows=_sample_rows(sh.n_tokens, seed=4))
+
+
+@pytest.mark.timeout(600)
 def test_decode_long_ctx():
     sh = synth.WORKLOADS["llama3-8b-long-ctx"].replace(name="llama3-8b-decode-1@32767",
                                                         n_tokens=1, start=32767)

@@ -372,23 +372,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
     }
 }
 
-// Merge of the split-KV partial results of one (query row, head): with M the
-// largest running max, o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-// The splits are spread over the block: threads take splits for the max and
-// the weights, then (head dim, split group) pairs for the weighted sum, so
-// the loads of different splits are in flight together.
+// Merge of the split-KV partial results for few (query row, head) pairs
+// (decode steps): one block per pair; threads take key ranges for the max and
+// the weights (block reductions), then (head dim, range group) pairs for the
+// weighted sum, so the loads of different ranges are in flight together.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ po,
-                                                          const float* __restrict__ pml,
-                                                          int n_split, int M, int nq,
-                                                          uint16_t* __restrict__ out, int out_ld) {
-  constexpr int G = 256 / HD;   // split groups of the weighted sum
+__global__ __launch_bounds__(256) void attn_combine_block_kernel(
+    const float* __restrict__ po, const float* __restrict__ pml, int n_split, int M, int nq,
+    uint16_t* __restrict__ out, int out_ld) {
+  constexpr int G = 256 / HD;   // range groups of the weighted sum
   __shared__ float wgt[kAttnMaxSplits];
   __shared__ float red[4];
   __shared__ float acc_g[256];
-  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const size_t row = static_cast<size_t>(t) * nq + h;         // within one split
-  const size_t sstride = static_cast<size_t>(M) * nq;         // between splits
+  const int pair = blockIdx.x, tid = threadIdx.x;
+  const size_t row = static_cast<size_t>(pair);
+  const size_t sstride = static_cast<size_t>(M) * nq;
   float mv = -INFINITY;
   for (int sp = tid; sp < n_split; sp += 256) mv = fmaxf(mv, pml[(sp * sstride + row) * 2]);
   mv = wave_max(mv);
@@ -413,8 +411,55 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     float o = 0.f;
 #pragma unroll
     for (int g2 = 0; g2 < G; ++g2) o += acc_g[g2 * HD + tid];
-    out[static_cast<size_t>(t) * out_ld + h * HD + tid] = f32_to_bf16(o / l);
+    out[static_cast<size_t>(pair / nq) * out_ld + (pair % nq) * HD + tid] = f32_to_bf16(o / l);
   }
+}
+
+// Merge of the split-KV partial results for many (query row, head) pairs
+// (prefill micro-batches): one wavefront per pair, four per block.  With M the largest running max,
+// o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  Lanes take key ranges
+// for the max and the weight sum (wavefront reductions), then head dims
+// (HD / 64 per lane) for the weighted sum of the range outputs, whose loads
+// are independent of each other.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ po,
+                                                          const float* __restrict__ pml,
+                                                          int n_split, int M, int nq,
+                                                          uint16_t* __restrict__ out, int out_ld) {
+  constexpr int DPL = HD / 64;   // head dims per lane
+  __shared__ float wgt_s[4][kAttnMaxSplits];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int pair = blockIdx.x * 4 + wv;           // (row, head), head fastest
+  if (pair >= M * nq) return;                     // whole wavefronts
+  const size_t row = static_cast<size_t>(pair);   // (t * nq + h) inside one split
+  const size_t sstride = static_cast<size_t>(M) * nq;
+  float* wgt = wgt_s[wv];
+  float mv = -INFINITY;
+  for (int sp = lane; sp < n_split; sp += 64) mv = fmaxf(mv, pml[(sp * sstride + row) * 2]);
+  const float m = wave_max(mv);
+  float lv = 0.f;
+  for (int sp = lane; sp < n_split; sp += 64) {
+    const float w = fast_exp2(pml[(sp * sstride + row) * 2] - m);
+    wgt[sp] = w;
+    lv += pml[(sp * sstride + row) * 2 + 1] * w;
+  }
+  const float l = wave_sum(lv);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // this wavefront's LDS writes of wgt[] are done
+  __builtin_amdgcn_wave_barrier();
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int sp = 0; sp < n_split; ++sp) {
+    const float w = wgt[sp];
+    const float* src = po + (sp * sstride + row) * HD + lane * DPL;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] += src[e] * w;
+  }
+  const float inv = 1.0f / l;
+  uint16_t* dst = out + static_cast<size_t>(pair / nq) * out_ld + (pair % nq) * HD + lane * DPL;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) dst[e] = f32_to_bf16(acc[e] * inv);
 }
 
 // fp32 kernel: one block per (query token, query head); keys in chunks of
@@ -493,7 +538,7 @@ static AttnGrid attn_grid(int M, int nq, int nkv) {
 int attention_kv_splits(int M, int kv_len, int nq, int nkv) {
   const AttnGrid g = attn_grid(M, nq, nkv);
   if (g.waves != 4 || g.blocks >= 256) return 1;   // the grid already fills the GPU
-  if (kv_len < 8 * M) return 1;   // keys mostly on the causal diagonal: ranges unbalanced
+  if (kv_len < 2 * M) return 1;   // keys mostly on the causal diagonal: ranges unbalanced
   const int nkb = (kv_len + 63) / 64;
   int ns = (512 + g.blocks - 1) / g.blocks;        // about 512 blocks in all
   if (ns > kAttnMaxSplits) ns = kAttnMaxSplits;
@@ -555,11 +600,19 @@ hipError_t launch_attention(Act act, bool kv16, const void* q, int q_ld, const v
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 cgrid(M, nq);
-    if (head_dim == 128)
-      attn_combine_kernel<128><<<cgrid, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
-    else
-      attn_combine_kernel<64><<<cgrid, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+    const int pairs = M * nq;
+    if (pairs < 1024) {   // few pairs: a whole block per pair
+      if (head_dim == 128)
+        attn_combine_block_kernel<128><<<pairs, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+      else
+        attn_combine_block_kernel<64><<<pairs, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+    } else {
+      const int cblocks = (pairs + 3) / 4;
+      if (head_dim == 128)
+        attn_combine_kernel<128><<<cblocks, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+      else
+        attn_combine_kernel<64><<<cblocks, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+    }
     return hipGetLastError();
   }
   dim3 grid(gr.blocks);
