@@ -85,6 +85,10 @@ SMALL = [
     _small("bf16-start0-long-rows", n_tokens=300, start=0, max_seq=300),
     _small("f32-g4-ragged", hidden=256, inter=344, n_tokens=70, start=9, max_seq=96,
            dtype="f32", qk_norm=True),
+    # I = 16384 at 512 tokens: 256x256 SwiGLU tiles fill one wave of blocks exactly,
+    # where 112-column tiles would spill into a second one
+    _small("bf16-swiglu-256tiles", hidden=256, inter=16384, nq=4, nkv=2, head_dim=64,
+           n_tokens=512, start=0, max_seq=512),
     # enough (kv head, 256-token) tiles to fill the GPU: eight-wavefront attention blocks
     _small("bf16-8wave-g1-hd64", hidden=256, inter=512, nq=32, nkv=32, head_dim=64,
            n_tokens=2000, start=37, max_seq=2048),
@@ -106,6 +110,12 @@ def test_small_layer_nonzero_index():
 def test_sign1_small_layer():
     _check_layer(_small("sign1-small", hidden=512, inter=1024, nq=4, nkv=2, n_tokens=96,
                         start=16, max_seq=128, qk_norm=True, eps=1e-6, wformat="sign1"))
+
+
+def test_sign1_decode_step():
+    # 1-bit weights keep the tiled GEMM for short micro-batches too
+    _check_layer(_small("sign1-decode", hidden=512, inter=1024, nq=4, nkv=2, n_tokens=1,
+                        start=700, max_seq=768, qk_norm=True, eps=1e-6, wformat="sign1"))
 
 
 # Decode steps and short batches (<= 32 rows): skinny projections, and split-KV
