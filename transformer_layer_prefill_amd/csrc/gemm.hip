@@ -687,13 +687,57 @@ constexpr int kMaxSplits = 8;
 
 static int big_tiles(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256); }
 
-int gemm_partial_splits(int M, int N, int K) {
-  const int tiles = big_tiles(M, N);
-  int splits = kCUs / tiles;   // the grid stays within one wave of work items
-  if (splits > kMaxSplits) splits = kMaxSplits;
+// Split-K plan of the Partial epilogue: tile width (256 or 128 columns, 256
+// rows either way) and slice count, about one work item per CU.  The next row
+// pass reads every slice once, so 256x128 tiles with half as many slices are
+// used where that pays: the output projection at the 8B shape (4 slices of
+// 256x128 instead of 8 of 256x256).
+struct PartialPlan {
+  int bn, splits;
+};
+// (the narrow tiles exist for the direct-to-LDS kernel only: dense weights, K % 64 == 0)
+static PartialPlan partial_plan(int M, int N, int K, bool narrow_ok) {
   const int k_tiles = (K + 63) / 64;
+  auto clamp = [&](int sp) { return sp < 1 ? 1 : (sp > k_tiles ? k_tiles : sp); };
+  const int narrow = ((M + 255) / 256) * ((N + 127) / 128);
+  int splits = kCUs / narrow;
+  // (measured: with fewer than 4 slices the narrow grid under-fills the GPU,
+  // and beyond K = 4096 its extra weight traffic per flop outweighs the
+  // slices it saves)
+  if (narrow_ok && splits >= 4 && K <= 4096)
+    return {128, clamp(splits > kMaxSplits ? kMaxSplits : splits)};
+  splits = kCUs / big_tiles(M, N);   // the grid stays within one wave of work items
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  return {256, clamp(splits)};
+}
+
+// the slice count run_bf16 ends up with (whole 64-wide K tiles per slice)
+static int slices_of(int K, int splits) {
+  const int k_tiles = (K + 63) / 64;
+  const int per = (k_tiles + splits - 1) / splits;
+  return (k_tiles + per - 1) / per;
+}
+
+int gemm_partial_splits(int M, int N, int K) {
+  // an upper bound over both plans (workspace sizing)
+  const int a = slices_of(K, partial_plan(M, N, K, true).splits);
+  const int b = slices_of(K, partial_plan(M, N, K, false).splits);
+  return a > b ? a : b;
+}
+
+// Partial epilogue with 256x128 tiles: the direct-to-LDS kernel only.
+template <bool OUT_F32>
+static hipError_t run_partial_narrow(GemmArgs g, int splits, hipStream_t s) {
+  g.m_tiles = (g.M + 255) / 256;
+  g.n_tiles = (g.N + 127) / 128;
+  const int k_tiles = g.K / 64;
   if (splits > k_tiles) splits = k_tiles;
-  return splits < 1 ? 1 : splits;
+  const int per = (k_tiles + splits - 1) / splits;
+  g.k_split = per * 64;
+  g.splits = (k_tiles + per - 1) / per;
+  if (g.splits_out) *g.splits_out = g.splits;
+  gemm_bf16_dma_kernel<256, 128, 2, 4, 4, OUT_F32><<<g.m_tiles * g.n_tiles * g.splits, 512, 0, s>>>(g);
+  return hipGetLastError();
 }
 
 // SwiGLU with dense weights and K % 64 == 0: 112-column tiles when they fill
@@ -722,7 +766,9 @@ static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
   const int cols_big = EPI == 2 ? 128 : 256;
   const long tiles_big = static_cast<long>((g.M + 255) / 256) * ((g.N + cols_big - 1) / cols_big);
   if (EPI == 4) {
-    return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, gemm_partial_splits(g.M, g.N, g.K), s);
+    const PartialPlan p = partial_plan(g.M, g.N, g.K, !SIGN1 && g.K % 64 == 0);
+    if (p.bn == 128) return run_partial_narrow<OUT_F32>(g, p.splits, s);
+    return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, p.splits, s);
   }
   if (tiles_big >= kCUs * 3 / 4) return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, 1, s);
   return run_bf16<128, 128, 2, 2, EPI, SIGN1, OUT_F32>(g, 1, s);
