@@ -699,6 +699,15 @@ struct PartialPlan {
 static PartialPlan partial_plan(int M, int N, int K, bool narrow_ok) {
   const int k_tiles = (K + 63) / 64;
   auto clamp = [&](int sp) { return sp < 1 ? 1 : (sp > k_tiles ? k_tiles : sp); };
+  // 192-column tiles when they split N exactly into a grid that, with its
+  // slices, fills the CUs with fewer slices than 256-column tiles
+  if (narrow_ok && N % 192 == 0) {
+    const int t192 = ((M + 255) / 256) * (N / 192);
+    const int sp192 = kCUs / t192;
+    const int sp256 = kCUs / big_tiles(M, N);
+    if (sp192 >= 2 && t192 * sp192 > big_tiles(M, N) * sp256)
+      return {192, clamp(sp192 > kMaxSplits ? kMaxSplits : sp192)};
+  }
   const int narrow = ((M + 255) / 256) * ((N + 127) / 128);
   int splits = kCUs / narrow;
   // (measured: with fewer than 4 slices the narrow grid under-fills the GPU,
@@ -725,18 +734,21 @@ int gemm_partial_splits(int M, int N, int K) {
   return a > b ? a : b;
 }
 
-// Partial epilogue with 256x128 tiles: the direct-to-LDS kernel only.
-template <bool OUT_F32>
+// Partial epilogue with 256x128 or 256x192 tiles: the direct-to-LDS kernel only.
+template <int BN, bool OUT_F32>
 static hipError_t run_partial_narrow(GemmArgs g, int splits, hipStream_t s) {
   g.m_tiles = (g.M + 255) / 256;
-  g.n_tiles = (g.N + 127) / 128;
+  g.n_tiles = (g.N + BN - 1) / BN;
   const int k_tiles = g.K / 64;
   if (splits > k_tiles) splits = k_tiles;
   const int per = (k_tiles + splits - 1) / splits;
   g.k_split = per * 64;
   g.splits = (k_tiles + per - 1) / per;
   if (g.splits_out) *g.splits_out = g.splits;
-  gemm_bf16_dma_kernel<256, 128, 2, 4, 4, OUT_F32><<<g.m_tiles * g.n_tiles * g.splits, 512, 0, s>>>(g);
+  if constexpr (BN == 192)   // 4 x 2 wavefronts of 64 x 96
+    gemm_bf16_dma_kernel<256, 192, 4, 2, 4, OUT_F32><<<g.m_tiles * g.n_tiles * g.splits, 512, 0, s>>>(g);
+  else
+    gemm_bf16_dma_kernel<256, 128, 2, 4, 4, OUT_F32><<<g.m_tiles * g.n_tiles * g.splits, 512, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -767,7 +779,8 @@ static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
   const long tiles_big = static_cast<long>((g.M + 255) / 256) * ((g.N + cols_big - 1) / cols_big);
   if (EPI == 4) {
     const PartialPlan p = partial_plan(g.M, g.N, g.K, !SIGN1 && g.K % 64 == 0);
-    if (p.bn == 128) return run_partial_narrow<OUT_F32>(g, p.splits, s);
+    if (p.bn == 128) return run_partial_narrow<128, OUT_F32>(g, p.splits, s);
+    if (p.bn == 192) return run_partial_narrow<192, OUT_F32>(g, p.splits, s);
     return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, p.splits, s);
   }
   if (tiles_big >= kCUs * 3 / 4) return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, 1, s);
