@@ -96,8 +96,9 @@ typedef struct {
 
 /* Weights of one layer (metal_prefill.rs LayerWeightRefs).  Gains are [H]
  * (q_norm/k_norm: [hd], shared by all heads; ignored unless qk_norm) in the
- * config's dtype.  Shapes: w_qkv [(nq+2nkv)hd][H] with Q rows, then K, then V;
- * w_o [H][nq*hd]; w_gate_up [2I][H] with the gate rows first; w_down [H][I]. */
+ * config's dtype, every gain 16-byte aligned.  Shapes: w_qkv [(nq+2nkv)hd][H]
+ * with Q rows, then K, then V; w_o [H][nq*hd]; w_gate_up [2I][H] with the
+ * gate rows first; w_down [H][I]. */
 typedef struct {
   const void* attn_norm;
   tlp_weight w_qkv;
@@ -149,7 +150,8 @@ tlp_status tlp_rope_table(double theta, int32_t head_dim, int32_t n_pos, float* 
  * in dtype (fp16 with TLP_KV_F16); exactly the slots [start_position, start_position + n_tokens) of
  * `layer` are written, slots [0, start_position + n_tokens) of `layer` are read,
  * and every slot below start_position must already hold that position's K/V.
- * rope_cos, rope_sin: device fp32 [>= start_position + n_tokens][hd/2].
+ * rope_cos, rope_sin: device fp32 [>= start_position + n_tokens][hd/2],
+ * 16-byte aligned.
  * workspace: device, >= tlp_workspace_bytes(cfg, n_tokens) bytes, 256-aligned. */
 tlp_status tlp_prefill_layer(const tlp_config* cfg, const tlp_layer_weights* weights,
                              int32_t layer, void* hidden, int32_t n_tokens,

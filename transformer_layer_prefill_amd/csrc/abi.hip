@@ -155,7 +155,8 @@ tlp_status check_layer_weights(const tlp_config& c, const tlp_layer_weights* w, 
     return fail(TLP_ERR_NULL, "layer %d: a norm gain is NULL", idx);
   if (c.qk_norm && (!w->q_norm || !w->k_norm))
     return fail(TLP_ERR_NULL, "layer %d: qk_norm is on but q_norm/k_norm is NULL", idx);
-  if (!aligned16(w->attn_norm) || !aligned16(w->ffn_norm))
+  if (!aligned16(w->attn_norm) || !aligned16(w->ffn_norm) ||
+      (c.qk_norm && (!aligned16(w->q_norm) || !aligned16(w->k_norm))))
     return fail(TLP_ERR_UNSUPPORTED, "layer %d: norm gains must be 16-byte aligned", idx);
   tlp_status s;
   if ((s = check_weight(c, w->w_qkv, "w_qkv")) != TLP_OK) return s;
@@ -174,8 +175,9 @@ tlp_status check_call(const tlp_config& c, void* hidden, int n, int start, void*
   if (static_cast<int64_t>(start) + n > c.max_seq)
     return fail(TLP_ERR_POSITION, "start_position %d + n_tokens %d exceeds max_seq %d", start,
                 n, c.max_seq);
-  if (!aligned16(hidden) || !aligned16(kc) || !aligned16(vc))
-    return fail(TLP_ERR_UNSUPPORTED, "hidden and caches must be 16-byte aligned");
+  if (!aligned16(hidden) || !aligned16(kc) || !aligned16(vc) || !aligned16(cs) ||
+      !aligned16(sn))
+    return fail(TLP_ERR_UNSUPPORTED, "hidden, caches and rope tables must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(ws) & 255)
     return fail(TLP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const size_t need = layout_of(c, m_ws).total;

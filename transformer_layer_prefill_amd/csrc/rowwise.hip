@@ -127,73 +127,151 @@ hipError_t launch_rownorm(Act act, const RowArgs& a, hipStream_t s) {
   return act == Act::F32 ? rownorm_t<float>(a, s) : rownorm_t<uint16_t>(a, s);
 }
 
-// Block (t, y) covers token t; its wave w takes head 4y + w of [Q heads | K heads | V heads].
-// Lane i owns the rotate-half pair (i, i + hd/2) of a Q/K head, so the head's
-// RMSNorm is a single wavefront reduction and RoPE needs no data exchange.
-// The projected row is either qkv itself (activation type) or, when the QKV
-// GEMM split K, the sum of its n_part fp32 slices; roped Q is written back into
-// qkv for the attention kernel either way.
-template <typename T, typename C>
+// E consecutive elements <-> floats (E = 2 or 4; the pointers are E-aligned).
+template <int E> __device__ __forceinline__ void ldv(const float* p, float (&x)[E]) {
+  if constexpr (E == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  } else {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    x[0] = v.x; x[1] = v.y;
+  }
+}
+template <int E> __device__ __forceinline__ void ldv(const uint16_t* p, float (&x)[E]) {
+  uint32_t w[E / 2];
+  if constexpr (E == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+#pragma unroll
+  for (int e = 0; e < E / 2; ++e) {
+    x[2 * e] = __uint_as_float(w[e] << 16);
+    x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+template <int E> __device__ __forceinline__ void stv(float* p, const float (&x)[E]) {
+  if constexpr (E == 4) *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  else *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+}
+template <int E> __device__ __forceinline__ void stv(uint16_t* p, const float (&x)[E]) {
+  if constexpr (E == 4) *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+  else *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(x[0], x[1]);
+}
+template <int E> __device__ __forceinline__ void stv(f16_t* p, const float (&x)[E]) {
+  uint32_t w[E / 2];
+#pragma unroll
+  for (int e = 0; e < E / 2; ++e)
+    w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<f16_t>(x[2 * e]))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<f16_t>(x[2 * e + 1]))) << 16);
+  if constexpr (E == 4) *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  else *reinterpret_cast<uint32_t*>(p) = w[0];
+}
+
+// Block (t, y) covers token t and heads 16y .. 16y+15 of [Q heads | K heads |
+// V heads]; a group of 16 lanes takes one head.  Lane j of a group owns the E
+// = hd/32 consecutive elements E*j .. of each rotate-half half, so every pair
+// (i, i + hd/2) stays in one lane, loads and stores are E-wide vectors, and
+// the head's RMSNorm is a 16-lane reduction.  The projected row is either qkv
+// itself (activation type) or, when the QKV GEMM split K, the sum of its
+// n_part fp32 slices; roped Q is written back into qkv for the attention
+// kernel either way, roped K and raw V go to the cache in its type C.
+template <typename T, typename C, int HD>
 __global__ __launch_bounds__(256) void qk_rope_store_kernel(
     T* __restrict__ qkv, int qkv_ld, const float* __restrict__ part, int n_part,
     size_t part_stride, const T* __restrict__ q_gain, const T* __restrict__ k_gain,
     int qk_norm, float eps, const float* __restrict__ rope_cos,
     const float* __restrict__ rope_sin, C* __restrict__ k_layer, C* __restrict__ v_layer,
-    int max_seq, int start, int nq, int nkv, int hd) {
+    int max_seq, int start, int nq, int nkv) {
+  constexpr int HALF = HD / 2, E = HALF / 16;
   const int t = blockIdx.x;
   const int pos = start + t;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = hd >> 1;
+  const int j = threadIdx.x & 15;
+  const int hh = blockIdx.y * 16 + (threadIdx.x >> 4);
+  if (hh >= nq + 2 * nkv) return;   // whole 16-lane groups; no block-wide sync follows
   T* row = qkv + static_cast<size_t>(t) * qkv_ld;
   const float* prow = part + static_cast<size_t>(t) * qkv_ld;
-  const int n_heads = nq + 2 * nkv;
-  auto in = [&](int col) -> float {
-    if (n_part == 0) return to_f32(row[col]);
+  const int c1 = hh * HD + E * j, c2 = c1 + HALF;
+  float x1[E], x2[E];
+  if (n_part == 0) {
+    ldv<E>(row + c1, x1);
+    ldv<E>(row + c2, x2);
+  } else {
     constexpr int MAXP = 8;   // issue every slice load before summing
-    float q[MAXP];
+    float q1[MAXP][E], q2[MAXP][E];
 #pragma unroll
-    for (int p = 0; p < MAXP; ++p) q[p] = p < n_part ? prow[p * part_stride + col] : 0.f;
-    float v = 0.f;
-#pragma unroll
-    for (int p = 0; p < MAXP; ++p) v += q[p];
-    return v;
-  };
-  for (int hh = blockIdx.y * 4 + wave; hh < n_heads; hh += gridDim.y * 4) {
-    if (hh >= nq + nkv) {  // V head: raw copy into the cache slot
-      const int j = hh - nq - nkv;
-      C* dst = v_layer + (static_cast<size_t>(j) * max_seq + pos) * hd;
-      for (int i = lane; i < hd; i += 64) dst[i] = from_f32<C>(in(hh * hd + i));
-      continue;
-    }
-    const bool active = lane < half;
-    float x1 = 0.f, x2 = 0.f;
-    if (active) {
-      x1 = in(hh * hd + lane);
-      x2 = in(hh * hd + lane + half);
-    }
-    if (qk_norm) {
-      const float ss = wave_sum(x1 * x1 + x2 * x2);
-      const float inv = rsqrtf(ss / static_cast<float>(hd) + eps);
-      const T* g = hh < nq ? q_gain : k_gain;
-      if (active) {
-        x1 = to_f32(g[lane]) * (x1 * inv);
-        x2 = to_f32(g[lane + half]) * (x2 * inv);
+    for (int p = 0; p < MAXP; ++p)
+      if (p < n_part) {
+        ldv<E>(prow + p * part_stride + c1, q1[p]);
+        ldv<E>(prow + p * part_stride + c2, q2[p]);
       }
-    }
-    if (!active) continue;
-    const float c = rope_cos[static_cast<size_t>(pos) * half + lane];
-    const float sn = rope_sin[static_cast<size_t>(pos) * half + lane];
-    const float y1 = x1 * c - x2 * sn;
-    const float y2 = x2 * c + x1 * sn;
-    if (hh < nq) {
-      row[hh * hd + lane] = from_f32<T>(y1);
-      row[hh * hd + lane + half] = from_f32<T>(y2);
-    } else {
-      C* dst = k_layer + (static_cast<size_t>(hh - nq) * max_seq + pos) * hd;
-      dst[lane] = from_f32<C>(y1);
-      dst[lane + half] = from_f32<C>(y2);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x1[e] = x2[e] = 0.f;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (p < n_part)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          x1[e] += q1[p][e];
+          x2[e] += q2[p][e];
+        }
+  }
+  if (hh >= nq + nkv) {  // V head: raw copy into the cache slot
+    C* dst = v_layer + (static_cast<size_t>(hh - nq - nkv) * max_seq + pos) * HD;
+    stv<E>(dst + E * j, x1);
+    stv<E>(dst + HALF + E * j, x2);
+    return;
+  }
+  if (qk_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 16);
+    const float inv = rsqrtf(ss / static_cast<float>(HD) + eps);
+    const T* g = hh < nq ? q_gain : k_gain;
+    float g1[E], g2[E];
+    ldv<E>(g + E * j, g1);
+    ldv<E>(g + HALF + E * j, g2);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      x1[e] = g1[e] * (x1[e] * inv);
+      x2[e] = g2[e] * (x2[e] * inv);
     }
   }
+  float cs[E], sn[E], y1[E], y2[E];
+  ldv<E>(rope_cos + static_cast<size_t>(pos) * HALF + E * j, cs);
+  ldv<E>(rope_sin + static_cast<size_t>(pos) * HALF + E * j, sn);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    y1[e] = x1[e] * cs[e] - x2[e] * sn[e];
+    y2[e] = x2[e] * cs[e] + x1[e] * sn[e];
+  }
+  if (hh < nq) {
+    stv<E>(row + c1, y1);
+    stv<E>(row + c2, y2);
+  } else {
+    C* dst = k_layer + (static_cast<size_t>(hh - nq) * max_seq + pos) * HD;
+    stv<E>(dst + E * j, y1);
+    stv<E>(dst + HALF + E * j, y2);
+  }
+}
+
+template <typename T, typename C>
+static void rope_launch(int head_dim, dim3 grid, hipStream_t s, void* qkv, int qkv_ld,
+                        const float* part, int n_part, size_t part_stride, const void* q_gain,
+                        const void* k_gain, bool qk_norm, float eps, const float* rope_cos,
+                        const float* rope_sin, void* k_layer, void* v_layer, int max_seq,
+                        int start, int nq, int nkv) {
+#define TLP_ROPE(HD_)                                                                        \
+  qk_rope_store_kernel<T, C, HD_><<<grid, 256, 0, s>>>(                                     \
+      static_cast<T*>(qkv), qkv_ld, part, n_part, part_stride, static_cast<const T*>(q_gain), \
+      static_cast<const T*>(k_gain), qk_norm ? 1 : 0, eps, rope_cos, rope_sin,              \
+      static_cast<C*>(k_layer), static_cast<C*>(v_layer), max_seq, start, nq, nkv)
+  if (head_dim == 128) TLP_ROPE(128);
+  else TLP_ROPE(64);
+#undef TLP_ROPE
 }
 
 hipError_t launch_qk_rope_store(Act act, bool kv16, void* qkv, int M, int qkv_ld, const float* part,
@@ -203,26 +281,20 @@ hipError_t launch_qk_rope_store(Act act, bool kv16, void* qkv, int M, int qkv_ld
                                 void* v_layer, int max_seq, int start, int nq, int nkv,
                                 int head_dim, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (n_part > 8) return hipErrorInvalidValue;
-  dim3 grid(M, (nq + 2 * nkv + 3) / 4), block(256);
+  if (n_part > 8 || (head_dim != 64 && head_dim != 128)) return hipErrorInvalidValue;
+  dim3 grid(M, (nq + 2 * nkv + 15) / 16);
   if (act == Act::F32)
-    qk_rope_store_kernel<float, float><<<grid, block, 0, s>>>(
-        static_cast<float*>(qkv), qkv_ld, part, n_part, part_stride,
-        static_cast<const float*>(q_gain), static_cast<const float*>(k_gain), qk_norm ? 1 : 0,
-        eps, rope_cos, rope_sin, static_cast<float*>(k_layer), static_cast<float*>(v_layer),
-        max_seq, start, nq, nkv, head_dim);
+    rope_launch<float, float>(head_dim, grid, s, qkv, qkv_ld, part, n_part, part_stride, q_gain,
+                              k_gain, qk_norm, eps, rope_cos, rope_sin, k_layer, v_layer, max_seq,
+                              start, nq, nkv);
   else if (kv16)
-    qk_rope_store_kernel<uint16_t, f16_t><<<grid, block, 0, s>>>(
-        static_cast<uint16_t*>(qkv), qkv_ld, part, n_part, part_stride,
-        static_cast<const uint16_t*>(q_gain), static_cast<const uint16_t*>(k_gain),
-        qk_norm ? 1 : 0, eps, rope_cos, rope_sin, static_cast<f16_t*>(k_layer),
-        static_cast<f16_t*>(v_layer), max_seq, start, nq, nkv, head_dim);
+    rope_launch<uint16_t, f16_t>(head_dim, grid, s, qkv, qkv_ld, part, n_part, part_stride,
+                                 q_gain, k_gain, qk_norm, eps, rope_cos, rope_sin, k_layer,
+                                 v_layer, max_seq, start, nq, nkv);
   else
-    qk_rope_store_kernel<uint16_t, uint16_t><<<grid, block, 0, s>>>(
-        static_cast<uint16_t*>(qkv), qkv_ld, part, n_part, part_stride,
-        static_cast<const uint16_t*>(q_gain), static_cast<const uint16_t*>(k_gain),
-        qk_norm ? 1 : 0, eps, rope_cos, rope_sin, static_cast<uint16_t*>(k_layer),
-        static_cast<uint16_t*>(v_layer), max_seq, start, nq, nkv, head_dim);
+    rope_launch<uint16_t, uint16_t>(head_dim, grid, s, qkv, qkv_ld, part, n_part, part_stride,
+                                    q_gain, k_gain, qk_norm, eps, rope_cos, rope_sin, k_layer,
+                                    v_layer, max_seq, start, nq, nkv);
   return hipGetLastError();
 }
 
