@@ -278,55 +278,79 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
         for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
     }
     // The next block's scores go to the MFMAs while this block's weights are
-    // computed on the VALUs; the schedule below interleaves the two streams
-    // (a wavefront issues in order).  The last iteration recomputes its own
-    // block, whose K slot is still intact.
-    scores(min(kb + 1, kb_hi - 1), s_next);
-    // (a key range of the split form may hide every key from a row so far)
-    const float neg_m = SPLIT && m_run == -INFINITY ? 0.f : -m_run;
-    V8 pf[4];   // B operand of step 2*hb + half: slots (lh, e) <- r = 8*half + e
+    // computed on the VALUs.  A wavefront issues in order, so the two streams
+    // are interleaved by hand: each group below issues one K fragment read
+    // for AK products ahead, one score MFMA and EX weights, and the
+    // scheduling fences keep the groups in that order (the compiler places
+    // the LDS waits).  The last iteration recomputes its own block, whose K
+    // slot is still intact.
+    const char* Kt = kring + (min(kb + 1, kb_hi - 1) % SK) * TILE;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 16; ++r) s_next[hb][r] = 0.f;
+    // product i: key half hb = i % 2 (two independent chains), k-step i / 2
+    auto kread = [&](int i) __attribute__((always_inline)) {
+      const int krow = (i % 2) * 32 + lr;
+      return *reinterpret_cast<const V8*>(Kt + krow * ROWB +
+                                          ((((i / 2) * 2 + lh) ^ swz_k(krow)) << 4));
+    };
+    constexpr int NQK = 2 * KS, AK = 4, EX = 32 / NQK;
+    V8 kf[AK + 1];
+#pragma unroll
+    for (int i = 0; i < AK; ++i) kf[i] = kread(i);
+    // (a key range of the split form may hide every key from a row so far)
+    const float neg_m = SPLIT && m_run == -INFINITY ? 0.f : -m_run;
+    V8 pf[4];   // B operand of step 2*hb + half: slots (lh, e) <- r = 8*half + e
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      if (i + AK < NQK) kf[(i + AK) % (AK + 1)] = kread(i + AK);
+      s_next[i % 2] = Ops::mma(kf[i % (AK + 1)], qf[i / 2], s_next[i % 2]);
+#pragma unroll
+      for (int e = i * EX; e < (i + 1) * EX; ++e) {
+        const int hb = e / 16, r = e % 16;
         pf[hb * 2 + (r >> 3)][r & 7] = Ops::cvt(fast_exp2(fmaf(s[hb][r], c, neg_m)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // O^T += V^T P^T.  Slot (lh, e) of step (hb, half) is key
+    // hb*32 + half*16 + 8*(e/4) + 4*lh + e%4, matching the score layout above;
+    // each run of four consecutive keys is one transposing read.  Product j
+    // takes head-dim block j % DB (independent chains) and step j / DB; its
+    // V^T fragment is read AV products ahead.
+    const char* Vt = vring + (kb % SV) * TILE;
+    auto vread = [&](int jj) __attribute__((always_inline)) {
+      const int dim = (jj % DB) * 32 + tr_dim, st = jj / DB;
+      const int r0 = (st >> 1) * 32 + (st & 1) * 16 + lh * 4 + tr_key, r1 = r0 + 8;
+      const uint2 lo = lds_read_tr16(Vt + r0 * ROWB + (((dim >> 3) ^ swz_v(r0)) << 4) +
+                                     (dim & 7) * 2);
+      const uint2 hi = lds_read_tr16(Vt + r1 * ROWB + (((dim >> 3) ^ swz_v(r1)) << 4) +
+                                     (dim & 7) * 2);
+      return __builtin_bit_cast(V8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
+    constexpr int NPV = 4 * DB, AV = 2;
+    V8 vf[AV + 1];
+#pragma unroll
+    for (int jj = 0; jj < AV; ++jj) vf[jj] = vread(jj);
     // the row sum takes the same bf16 weights the products use, two per dot2
     float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 u = __builtin_bit_cast(uint4, pf[i]);
+    for (int q = 0; q < 4; ++q) {
+      const uint4 u = __builtin_bit_cast(uint4, pf[q]);
       psum0 = Ops::sum2(u.x, psum0);
       psum1 = Ops::sum2(u.y, psum1);
       psum0 = Ops::sum2(u.z, psum0);
       psum1 = Ops::sum2(u.w, psum1);
     }
     l_run += psum0 + psum1;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // 4 K fragment reads ahead
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
-      if (i + 4 < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one score MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU instructions
-    }
-
-    // O^T += V^T P^T.  Slot (lh, e) of step (hb, half) is key
-    // hb*32 + half*16 + 8*(e/4) + 4*lh + e%4, matching the score layout above;
-    // each run of four consecutive keys is one transposing read.
-    const char* Vt = vring + (kb % SV) * TILE;
-#pragma unroll
-    for (int d = 0; d < DB; ++d) {
-      const int dim = d * 32 + tr_dim;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kbase_r = (st >> 1) * 32 + (st & 1) * 16 + lh * 4 + tr_key;
-        const int r0 = kbase_r, r1 = kbase_r + 8;
-        const uint2 lo = lds_read_tr16(Vt + r0 * ROWB + (((dim >> 3) ^ swz_v(r0)) << 4) +
-                                       (dim & 7) * 2);
-        const uint2 hi = lds_read_tr16(Vt + r1 * ROWB + (((dim >> 3) ^ swz_v(r1)) << 4) +
-                                       (dim & 7) * 2);
-        const V8 vf = __builtin_bit_cast(V8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[d] = Ops::mma(vf, pf[st], o[d]);
-      }
+    for (int jj = 0; jj < NPV; ++jj) {
+      if (jj + AV < NPV) vf[(jj + AV) % (AV + 1)] = vread(jj + AV);
+      o[jj % DB] = Ops::mma(vf[jj % (AV + 1)], pf[jj / DB], o[jj % DB]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
