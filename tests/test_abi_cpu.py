@@ -53,12 +53,13 @@ def _weights(null=None):
     return w
 
 
-def _layer(cfg, w=None, layer=0, n=4, start=0, ws_bytes=None, hidden=FAKE, ws=FAKE, kc=FAKE):
+def _layer(cfg, w=None, layer=0, n=4, start=0, ws_bytes=None, hidden=FAKE, ws=FAKE, kc=FAKE,
+           rope=FAKE):
     w = w if w is not None else _weights()
     wsb = tlp.workspace_bytes(cfg, max(n, 1)) if ws_bytes is None else ws_bytes
     L = tlp.lib()
     st = L.tlp_prefill_layer(ctypes.byref(cfg), ctypes.byref(w), layer, hidden, n, start, kc,
-                             FAKE, FAKE, FAKE, ws, wsb, None)
+                             FAKE, rope, FAKE, ws, wsb, None)
     return st, L.tlp_last_error().decode()
 
 
@@ -95,6 +96,11 @@ def test_call_argument_checks():
     assert st == tlp.TLP_ERR_WORKSPACE and str(need) in msg
     for k in ("attn_norm", "ffn_norm", "w_qkv", "w_o", "w_gate_up", "w_down", "q_norm"):
         assert _layer(cfg, w=_weights(null=k))[0] == tlp.TLP_ERR_NULL, k
+    # the RoPE/KV kernel reads gains and rope tables with vector loads
+    assert _layer(cfg, rope=FAKE + 4)[0] == tlp.TLP_ERR_UNSUPPORTED
+    w = _weights()
+    w.q_norm = FAKE + 8
+    assert _layer(cfg, w=w)[0] == tlp.TLP_ERR_UNSUPPORTED
     # q_norm may be NULL when QK-norm is off
     cfg_off = _cfg(qk_norm=0)
     assert _layer(cfg_off, w=_weights(null="q_norm"), n=0)[0] == tlp.TLP_ERR_SHAPE
