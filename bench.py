@@ -289,7 +289,7 @@ def main():
                              "llama3-8b-verify-tail", "llama3-8b-stack32", "tiny-f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-f16", action="store_true",
-                    help="keep the KV cache in IEEE fp16 (the pages' cache type)")
+                    help="keep the KV cache in IEEE fp16 (the cache type of metal_full_layer.rs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times "
                          "(the calibration kernel for HBM traffic counters), then exit")
@@ -298,8 +298,8 @@ def main():
         copy_probe(args.copy_probe_mib)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
-              "sharding of this path is a design in DESIGN.md, not a measured run",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); sharding the "
+              "layer over several GPUs is not built, so there is no multi-GPU run",
               file=sys.stderr)
         sys.exit(2)
 

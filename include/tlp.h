@@ -58,8 +58,8 @@ typedef enum { TLP_F32 = 0, TLP_BF16 = 1 } tlp_dtype;
 /* Projection weight format.
  * TLP_W_DENSE: [N][K] in the config's dtype.
  * TLP_W_SIGN1_G128: 1-bit signs plus one fp16 scale per 128 consecutive
- *   weights of a row (the pages only name a structure-of-arrays 1-bit layout;
- *   this library fixes the format): `data` is uint32 [N][K/32] where bit b of
+ *   weights of a row (metal_prefill.rs only names a structure-of-arrays 1-bit
+ *   layout; this library fixes the format): `data` is uint32 [N][K/32] where bit b of
  *   word w is the sign of column 32w+b, least-significant bit first, 1 = +1 and
  *   0 = -1; `scales` is IEEE fp16 [N][K/128].  W[n][k] = scales[n][k/128] * sign.
  *   Requires K % 128 == 0 and dtype TLP_BF16. */
@@ -216,7 +216,7 @@ enum { TLP_K_ATTN_NORM = 0, TLP_K_QKV_GEMM = 1, TLP_K_QK_ROPE_KV = 2, TLP_K_ATTE
        TLP_K_ARGMAX = 12, TLP_K_COUNT = 13 };
 
 /* Per-kernel GPU timing, the analog of the per-layer / per-command-buffer
- * profiling switches of the pages (metal_full_layer.rs OXIBONSAI_PROFILE and
+ * profiling switches of metal_full_layer.rs (OXIBONSAI_PROFILE and
  * OXIBONSAI_PROFILE_GPU).  After tlp_profile_begin, every kernel launched by
  * this thread's tlp_prefill_* calls is bracketed by two HIP events recorded on
  * the call's stream.  tlp_profile_end waits for those events, writes the

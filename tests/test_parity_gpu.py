@@ -136,7 +136,7 @@ def test_decode_layer(shape):
     _check_layer(shape)
 
 
-# fp16 KV cache (the pages' cache type): K and V rounded to IEEE half when
+# fp16 KV cache (the cache type of metal_full_layer.rs): K and V rounded to IEEE half when
 # stored, attention on fp16 MFMAs
 KV16 = [
     _small("kv16-g4-ragged", kv="f16"),

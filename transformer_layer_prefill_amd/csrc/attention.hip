@@ -1,7 +1,7 @@
 // Causal grouped-query attention over the KV cache for every query row of a
 // micro-batch at once (oxibonsai-kernels metal_prefill.rs, encode_layer_prefill
 // step 3e: scores q.K/sqrt(hd) over seq_len = pos + 1 keys, softmax, weighted
-// sum of V; query head h reads kv head h / heads_per_group).  The pages run it
+// sum of V; query head h reads kv head h / heads_per_group).  That page runs it
 // one query position at a time with a materialised score row; here it is one
 // flash-style kernel with an online softmax and no score buffer.
 //

@@ -2,7 +2,8 @@
 // branch of encode_full_forward_prefill's tail, which dispatches an argmax
 // over the logits and returns one u32 token id instead of the logits, and
 // the per-position argmax of encode_full_forward_prefill_verify's tail).
-// The kernel body is not on the pages; ties go to the lowest index.
+// That page does not show the argmax kernel's body; here ties go to the
+// lowest index.
 #include <climits>
 
 #include "common.h"
