@@ -264,11 +264,14 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   const bool split = act == Act::BF16;
   const bool skinny = skinny_path(c, n);
 
-  // 1. residual assembly + attention RMSNorm
+  // 1. residual assembly + attention RMSNorm.  Rows that arrive in bf16 with
+  // no slices to add need no fp32 copy yet: widening bf16 is exact, so the
+  // FFN norm pass reads the same rows itself and writes the stream then.
+  const bool defer_res = split && !x_in_f32 && in_parts == 0;
   RowArgs r{};
   r.x = x_in; r.x_f32 = x_in_f32; r.ldx = H;
   r.part = part; r.n_part = in_parts; r.part_stride = part_stride;
-  r.res_out = res;
+  r.res_out = defer_res ? nullptr : res;
   r.gain = w.attn_norm; r.norm_out = xn;
   r.rows = n; r.H = H; r.eps = c.rms_eps;
   TLP_LAUNCH(TLP_K_ATTN_NORM, launch_rownorm(act, r, s));
@@ -326,7 +329,8 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   }
   // 5. residual assembly + FFN RMSNorm
   r = RowArgs{};
-  r.x = res; r.x_f32 = 1; r.ldx = H;
+  if (defer_res) { r.x = x_in; r.x_f32 = 0; } else { r.x = res; r.x_f32 = 1; }
+  r.ldx = H;
   r.part = part; r.n_part = o_parts; r.part_stride = part_stride;
   r.res_out = res;
   r.gain = w.ffn_norm; r.norm_out = xn;
