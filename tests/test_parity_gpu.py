@@ -31,12 +31,14 @@ def _inputs(shape, layer=0):
     return w, x, kc, vc
 
 
-def _check_layer(shape, rows=None, layer=0, label=""):
+def _check_layer(shape, rows=None, layer=0, label="", transform=None):
     log(f"[parity] {label or shape.name}: M={shape.n_tokens} start={shape.start} "
         f"H={shape.hidden} I={shape.inter} nq={shape.nq} nkv={shape.nkv} hd={shape.head_dim} "
         f"qk_norm={shape.qk_norm} dtype={shape.dtype} w={shape.wformat}")
     sh = shape.replace(n_layers=max(shape.n_layers, layer + 1))
     w, x, kc, vc = _inputs(sh, layer)
+    if transform is not None:
+        w = transform(w)
     gpu = GpuRun(sh, [w] * (layer + 1), x, kc, vc)
     gpu.layer(layer, sh.n_tokens, sh.start)
     g_hidden = synth.widen(gpu.host(gpu.hidden), sh.dtype)
@@ -110,6 +112,24 @@ def test_small_layer_nonzero_index():
 def test_sign1_small_layer():
     _check_layer(_small("sign1-small", hidden=512, inter=1024, nq=4, nkv=2, n_tokens=96,
                         start=16, max_seq=128, qk_norm=True, eps=1e-6, wformat="sign1"))
+
+
+def _negate_some_scales(w):
+    # the format allows any fp16 scale; the synthetic ones are all positive
+    rng = np.random.default_rng(77)
+    out = dict(w)
+    for k in ("w_qkv", "w_o", "w_gate_up", "w_down"):
+        sc = w[k]["scales"].copy()
+        flip = rng.random(sc.shape) < 0.5
+        sc[flip] = -sc[flip]
+        out[k] = {"bits": w[k]["bits"], "scales": sc}
+    return out
+
+
+def test_sign1_negative_scales():
+    _check_layer(_small("sign1-negative-scales", hidden=512, inter=1024, nq=4, nkv=2,
+                        n_tokens=96, start=16, max_seq=128, qk_norm=True, eps=1e-6,
+                        wformat="sign1"), transform=_negate_some_scales)
 
 
 def test_sign1_decode_step():

@@ -208,8 +208,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
         const int c = tid + i * T;
         const int r = c >> 1, wd = c & 1;
         // +scale for a set bit, -scale for a clear one, as bf16 bit patterns
+        // (negating flips the sign bit, whatever the sign of the scale)
         const uint32_t pos = s_ok[i] ? f32_to_bf16(f16_to_f32(s_scale[i])) : 0u;
-        const uint32_t neg = s_ok[i] ? (pos | 0x8000u) : 0u;
+        const uint32_t neg = s_ok[i] ? (pos ^ 0x8000u) : 0u;
         const uint32_t w = s_word[i];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
