@@ -104,6 +104,13 @@ def test_small_layer(shape):
     _check_layer(shape)
 
 
+def test_small_layer_swiglu112_tiles():
+    # 300 tokens and I = 12800: 2 x 115 blocks of 112 output columns win over
+    # 96-column tiles (2 x 134 > 256 blocks) and 256x256 tiles; ragged M and N
+    _check_layer(_small("bf16-swiglu112-ragged", hidden=256, inter=12800, nq=4, nkv=2,
+                        n_tokens=300, start=11, max_seq=320))
+
+
 def test_small_layer_nonzero_index():
     # layer 2 of a 3-layer cache: offsets into the cache by layer
     _check_layer(_small("bf16-layer2", n_tokens=40, start=3, max_seq=64, n_layers=3), layer=2)

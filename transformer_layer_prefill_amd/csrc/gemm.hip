@@ -432,30 +432,57 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
   gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh, split);
 }
 
-// ---- gate/up + SwiGLU with 112-column output tiles -----------------------------
-// A block covers 256 token rows and 112 output columns, i.e. 224 weight rows:
-// each of the two wavefront columns holds 56 gate and 56 up rows interleaved
-// eight by eight.  A 512-token micro-batch of an I = 14336 FFN then makes
-// 2 x 128 = 256 blocks, one per CU, where 256x256 tiles make 224 and leave 32
-// CUs idle.  Eight wavefronts of 64 rows x 112 weight rows use
-// v_mfma_f32_16x16x32_bf16 (4 x 7 fragments of 16x16); K tiles of 64 are
-// copied global -> LDS with global_load_lds_dwordx4 into a double buffer and
-// read with the same row swizzle as the 256x256 kernel.  In the 16x16 result
-// layout lane l holds column l % 16 of its fragment, so the gate value of an
-// output column sits eight lanes away from its up value.
-__device__ __forceinline__ void swiglu112_b_row(const GemmArgs& g, int nt, int rr, int& w_row) {
-  const int wn = rr / 112, q = rr % 112;
-  const int idx = min(nt * 112 + wn * 56 + 8 * (q / 16) + (q & 7), g.N - 1);
-  w_row = (q & 8) ? g.up_row + idx : idx;
+// ---- gate/up + SwiGLU with 112- or 96-column output tiles ----------------------
+// A block covers 256 token rows and COLS output columns, i.e. 2*COLS weight
+// rows: each of the two wavefront columns holds COLS/2 gate and COLS/2 up rows
+// interleaved eight by eight.  A 512-token micro-batch makes 2 x (I / COLS)
+// blocks: 256 (one per CU) for I = 14336 with 112 columns and for I = 12288
+// with 96, where 256x256 tiles make 224 and 192 and leave CUs idle.  Eight
+// wavefronts of 64 rows x 2*COLS/2 weight rows use v_mfma_f32_16x16x32_bf16
+// (4 x COLS/16 fragments of 16x16); K tiles of 64 are read from LDS with the
+// same row swizzle as the 256x256 kernel.  In the 16x16 result layout lane l
+// holds column l % 16 of its fragment, so the gate value of an output column
+// sits eight lanes away from its up value.
+//
+// Dense weights: both tiles are copied global -> LDS with global_load_lds_dwordx4
+// into a double buffer.  1-bit weights: the activation tile is copied the same
+// way; thread i < 4*COLS owns (weight row i/2, 32-column word i%2) of the tile,
+// loads its sign word and group scale two tiles ahead into registers and, right
+// after the barrier that frees a stage, expands them into bf16 +-scale in that
+// stage (K % 128 == 0: a 64-wide tile lies inside one scale group).  The
+// barrier of the next iteration publishes the expanded tile before its reads.
+template <int COLS>
+__device__ __forceinline__ int swiglu_b_row(const GemmArgs& g, int nt, int rr) {
+  const int wn = rr / COLS, q = rr % COLS;
+  const int idx = min(nt * COLS + wn * (COLS / 2) + 8 * (q / 16) + (q & 7), g.N - 1);
+  return (q & 8) ? g.up_row + idx : idx;
 }
 
-__global__ __launch_bounds__(512) void gemm_swiglu112_kernel(GemmArgs g) {
-  constexpr int BM = 256, BR = 224, BK = 64, ROWB = 128;
-  constexpr int FM = 4, FN = 7;                             // 16x16 fragments per wavefront
-  constexpr int A_BYTES = BM * ROWB, B_BYTES = BR * ROWB;   // 32 KB + 28 KB
+// 8 bf16 weights from 8 sign bits (bit e -> element e; 1 -> +scale, 0 ->
+// -scale) and the bf16 bit pattern of the scale: negating flips the sign bit.
+__device__ __forceinline__ uint4 sign1_expand8(uint32_t bits8, uint32_t sbf) {
+  const uint32_t ss = sbf | (sbf << 16);
+  const uint32_t neg = ~bits8 & 0xffu;
+  const uint32_t x2 = neg | (neg << 15);   // neg bit e at e, neg bit e at e + 15
+  uint4 u;
+  u.x = ss ^ ((x2 << 15) & 0x80008000u);
+  u.y = ss ^ ((x2 << 13) & 0x80008000u);
+  u.z = ss ^ ((x2 << 11) & 0x80008000u);
+  u.w = ss ^ ((x2 << 9) & 0x80008000u);
+  return u;
+}
+
+template <int COLS, bool SIGN1>
+__global__ __launch_bounds__(512) void gemm_swiglu_kernel(GemmArgs g) {
+  constexpr int BM = 256, BR = 2 * COLS, BK = 64, ROWB = 128;
+  constexpr int FM = 4, FN = COLS / 16;                     // 16x16 fragments per wavefront
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BR * ROWB;   // 32 KB + 28 or 24 KB
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_PW = 4, B_PW = 4;                         // DMA blocks per wavefront
-  constexpr int B_BLK = B_BYTES / 1024;                     // 28: wavefront 7 copies no B
+  constexpr int A_PW = 4;                                   // DMA blocks per wavefront
+  constexpr int B_BLK = B_BYTES / 1024;                     // 28 or 24
+  constexpr int B_PW = (B_BLK + 7) / 8;                     // 4 (wavefront 7 copies no B) or 3
+  constexpr int S_ITEMS = 2 * BR;                           // 1-bit: (row, word) pairs per tile
+  static_assert(COLS % 16 == 0 && S_ITEMS <= 512 && S_ITEMS % 64 == 0, "tile shape");
   typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
@@ -468,32 +495,63 @@ __global__ __launch_bounds__(512) void gemm_swiglu112_kernel(GemmArgs g) {
   const int l16 = lane & 15, lq = lane >> 4;
 
   const int drow = lane >> 3, dslot = lane & 7;
-  const uint16_t* W = static_cast<const uint16_t*>(g.W);
   const uint16_t* a_src[A_PW];
-  const uint16_t* b_src[B_PW];
 #pragma unroll
   for (int j = 0; j < A_PW; ++j) {
     const int row = (wave * A_PW + j) * 8 + drow;
     a_src[j] = g.A + static_cast<size_t>(min(m0 + row, g.M - 1)) * g.lda + (dslot ^ swz8(row)) * 8;
   }
-#pragma unroll
-  for (int j = 0; j < B_PW; ++j) {
-    const int rr = min((wave * B_PW + j) * 8 + drow, BR - 1);
-    int w_row;
-    swiglu112_b_row(g, nt, rr, w_row);
-    b_src[j] = W + static_cast<size_t>(w_row) * g.K + (dslot ^ swz8(rr)) * 8;
-  }
+  const uint16_t* b_src[SIGN1 ? 1 : B_PW];
   const bool has_b = wave * B_PW < B_BLK;   // wavefront-uniform
+  if constexpr (!SIGN1) {
+    const uint16_t* W = static_cast<const uint16_t*>(g.W);
+#pragma unroll
+    for (int j = 0; j < B_PW; ++j) {
+      const int rr = min((wave * B_PW + j) * 8 + drow, BR - 1);
+      b_src[j] = W + static_cast<size_t>(swiglu_b_row<COLS>(g, nt, rr)) * g.K + (dslot ^ swz8(rr)) * 8;
+    }
+  }
+  // 1-bit: this thread's (row, word) item; S_ITEMS is a multiple of 64, so
+  // ownership is wavefront-uniform
+  const bool s_own = SIGN1 && tid < S_ITEMS;
+  const int s_row = min(tid >> 1, BR - 1), s_wd = tid & 1;
+  const uint32_t* s_wsrc = nullptr;
+  const uint16_t* s_ssrc = nullptr;
+  if constexpr (SIGN1) {
+    const size_t wr = static_cast<size_t>(swiglu_b_row<COLS>(g, nt, s_row));
+    s_wsrc = static_cast<const uint32_t*>(g.W) + wr * (g.K >> 5) + s_wd;
+    s_ssrc = g.Wscale + wr * (g.K >> 7);
+  }
+  const int s_off = A_BYTES + s_row * ROWB;
+  const int s_sw = swz8(s_row);
+
   auto issue = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     char* st = smem + (kt & 1) * STAGE;
 #pragma unroll
     for (int j = 0; j < A_PW; ++j) dma16(a_src[j] + k0, st + (wave * A_PW + j) * 1024);
-    if (has_b) {
+    if constexpr (!SIGN1) {
+      if (has_b) {
 #pragma unroll
-      for (int j = 0; j < B_PW; ++j)
-        dma16(b_src[j] + k0, st + A_BYTES + (wave * B_PW + j) * 1024);
+        for (int j = 0; j < B_PW; ++j)
+          dma16(b_src[j] + k0, st + A_BYTES + (wave * B_PW + j) * 1024);
+      }
     }
+  };
+  auto load_s = [&](int kt, uint32_t& word, uint32_t& scale) __attribute__((always_inline)) {
+    const int k0 = kt * BK;
+    word = s_wsrc[k0 >> 5];
+    scale = s_ssrc[k0 >> 7];
+  };
+  // expand this thread's word of tile kt into its stage: columns 32*s_wd ..
+  // +32 of row s_row are the four 16-byte chunks 4*s_wd + q
+  auto store_s = [&](int kt, uint32_t word, uint32_t scale) __attribute__((always_inline)) {
+    char* st = smem + (kt & 1) * STAGE + s_off;
+    const uint32_t sbf = f32_to_bf16(f16_to_f32(static_cast<uint16_t>(scale)));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(st + (((4 * s_wd + q) ^ s_sw) << 4)) =
+          sign1_expand8((word >> (8 * q)) & 0xffu, sbf);
   };
 
   f32x4 acc[FM][FN];
@@ -504,7 +562,7 @@ __global__ __launch_bounds__(512) void gemm_swiglu112_kernel(GemmArgs g) {
 
   // fragment rows are 16-aligned, so every row this lane reads has swz8(l16)
   const int sw = swz8(l16);
-  const int a_off = (wm * 64 + l16) * ROWB, b_off = A_BYTES + (wn * 112 + l16) * ROWB;
+  const int a_off = (wm * 64 + l16) * ROWB, b_off = A_BYTES + (wn * COLS + l16) * ROWB;
   const int ch0 = ((0 * 4 + lq) ^ sw) << 4, ch1 = ((1 * 4 + lq) ^ sw) << 4;
   bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
 #define TLP_FRAGS16(AF, BF, ST, C)                                                           \
@@ -521,13 +579,31 @@ __global__ __launch_bounds__(512) void gemm_swiglu112_kernel(GemmArgs g) {
   // during the MFMAs of step 0, and the barrier + refill of the stage sit
   // between the two MFMA groups
   const int nk = g.K / BK;
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 1) {
-    if (has_b) __builtin_amdgcn_s_waitcnt(VmWait<A_PW + B_PW>::imm);
-    else __builtin_amdgcn_s_waitcnt(VmWait<A_PW>::imm);
-  } else {
+  uint32_t s_word = 0, s_scale = 0;   // 1-bit: tile kt+2's item, in flight during tile kt
+  if constexpr (SIGN1) {
+    // tiles 0 and 1 are expanded before the first barrier
+    uint32_t w0 = 0, c0 = 0, w1 = 0, c1 = 0;
+    issue(0);
+    if (s_own) load_s(0, w0, c0);
+    if (nk > 1) {
+      issue(1);
+      if (s_own) load_s(1, w1, c1);
+    }
     __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+    if (s_own) {
+      store_s(0, w0, c0);
+      if (nk > 1) store_s(1, w1, c1);
+      if (nk > 2) load_s(2, s_word, s_scale);
+    }
+  } else {
+    issue(0);
+    if (nk > 1) issue(1);
+    if (nk > 1) {
+      if (has_b) __builtin_amdgcn_s_waitcnt(VmWait<A_PW + B_PW>::imm);
+      else __builtin_amdgcn_s_waitcnt(VmWait<A_PW>::imm);
+    } else {
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+    }
   }
   lds_barrier();
   TLP_FRAGS16(af0, bf0, smem, ch0)
@@ -540,9 +616,19 @@ __global__ __launch_bounds__(512) void gemm_swiglu112_kernel(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);
     TLP_MMA16(af0, bf0)
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // tile kt+1, the only copy in flight
+    // tile kt+1 (its copy, and for 1-bit the item of tile kt+2) has landed
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
     lds_barrier();
-    if (kt + 2 < nk) issue(kt + 2);
+    // every read of tile kt is done: its stage takes tile kt+2
+    if (kt + 2 < nk) {
+      issue(kt + 2);
+      if constexpr (SIGN1) {
+        if (s_own) {
+          store_s(kt + 2, s_word, s_scale);
+          if (kt + 3 < nk) load_s(kt + 3, s_word, s_scale);
+        }
+      }
+    }
     const char* st1 = smem + ((kt + 1) & 1) * STAGE;
     TLP_FRAGS16(af0, bf0, st1, ch0)
     __builtin_amdgcn_sched_barrier(0);
@@ -571,7 +657,7 @@ __global__ __launch_bounds__(512) void gemm_swiglu112_kernel(GemmArgs g) {
         const float v = acc[i][j][r];
         const float up = __shfl_xor(v, 8, 64);
         const int m = m0 + wm * 64 + i * 16 + 4 * lq + r;
-        const int idx = nt * 112 + wn * 56 + 8 * j + l16;
+        const int idx = nt * COLS + wn * (COLS / 2) + 8 * j + l16;
         if (l16 < 8 && m < g.M && idx < g.N)
           out[static_cast<size_t>(m) * g.ldo + idx] = f32_to_bf16(silu_f32(v) * up);
       }
@@ -753,29 +839,43 @@ static hipError_t run_partial_narrow(GemmArgs g, int splits, hipStream_t s) {
   return hipGetLastError();
 }
 
-// SwiGLU with dense weights and K % 64 == 0: 112-column tiles when they fill
-// whole waves of 256 blocks better than 128-column (256x256) tiles do.  Work
-// per block is 7/8 of a 256x256 tile, so compare waves x work.
-static bool use_swiglu112(const GemmArgs& g) {
-  if (g.K % 64) return false;
+// SwiGLU with K % 64 == 0 (always so for 1-bit weights): output columns per
+// block, 128 (256x256 tiles), 112 or 96, whichever needs the fewest waves of
+// 256 blocks times the work per block (COLS/128 of a 256x256 tile); ties keep
+// the wider tile.  At 512 tokens: 112 for I = 14336, 96 for I = 12288.
+static int swiglu_cols(const GemmArgs& g) {
+  if (g.K % 64) return 128;
   const long mt = (g.M + 255) / 256;
-  const long t128 = mt * ((g.N + 127) / 128), t112 = mt * ((g.N + 111) / 112);
-  const long w128 = (t128 + kCUs - 1) / kCUs, w112 = (t112 + kCUs - 1) / kCUs;
-  return w112 * 7 < w128 * 8;
+  int best = 128;
+  long best_cost = 0;
+  for (int c : {128, 112, 96}) {
+    const long tiles = mt * ((g.N + c - 1) / c);
+    const long cost = ((tiles + kCUs - 1) / kCUs) * c;
+    if (c == 128 || cost < best_cost) {
+      best = c;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
-static hipError_t run_swiglu112(GemmArgs g, hipStream_t s) {
+template <int COLS, bool SIGN1>
+static hipError_t run_swiglu_narrow(GemmArgs g, hipStream_t s) {
   g.m_tiles = (g.M + 255) / 256;
-  g.n_tiles = (g.N + 111) / 112;
+  g.n_tiles = (g.N + COLS - 1) / COLS;
   g.splits = 1;
   g.k_split = g.K;
-  gemm_swiglu112_kernel<<<g.m_tiles * g.n_tiles, 512, 0, s>>>(g);
+  gemm_swiglu_kernel<COLS, SIGN1><<<g.m_tiles * g.n_tiles, 512, 0, s>>>(g);
   return hipGetLastError();
 }
 
 template <int EPI, bool SIGN1, bool OUT_F32>
 static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
-  if (EPI == 2 && !SIGN1 && !OUT_F32 && use_swiglu112(g)) return run_swiglu112(g, s);
+  if constexpr (EPI == 2 && !OUT_F32) {
+    const int cols = swiglu_cols(g);
+    if (cols == 112) return run_swiglu_narrow<112, SIGN1>(g, s);
+    if (cols == 96) return run_swiglu_narrow<96, SIGN1>(g, s);
+  }
   const int cols_big = EPI == 2 ? 128 : 256;
   const long tiles_big = static_cast<long>((g.M + 255) / 256) * ((g.N + cols_big - 1) / cols_big);
   if (EPI == 4) {
