@@ -4,10 +4,11 @@
 // projection with residual, the fused gate+up+SwiGLU GEMM and the down
 // projection with residual).  Both operands are K-contiguous, tokens are rows.
 //
-// bf16 path: CDNA4 v_mfma_f32_32x32x16_bf16, fp32 accumulation, LDS-staged
-// double-buffered tiles with register prefetch, XCD-aware tile order.
-// 1-bit path: the same kernel with the weight tile expanded from packed sign
-// bits and an fp16 group scale into bf16 while it is staged into LDS.
+// bf16 path: CDNA4 bf16 MFMAs with fp32 accumulation; tiles copied global ->
+// LDS by DMA into a double buffer (register-staged when K is not a multiple
+// of 64), XCD-aware tile order.
+// 1-bit path: the same direct-to-LDS kernels; the threads expand each weight
+// tile from packed sign bits and an fp16 group scale into bf16 in LDS.
 // fp32 path: a plain LDS-tiled FMA kernel (small correctness shapes).
 #include "common.h"
 #include "launch.h"
@@ -39,6 +40,20 @@ __device__ __forceinline__ uint4 keep_if(uint4 v, bool ok) {
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// 8 bf16 weights from 8 sign bits (bit e -> element e; 1 -> +scale, 0 ->
+// -scale) and the bf16 bit pattern of the scale: negating flips the sign bit.
+__device__ __forceinline__ uint4 sign1_expand8(uint32_t bits8, uint32_t sbf) {
+  const uint32_t ss = sbf | (sbf << 16);
+  const uint32_t neg = ~bits8 & 0xffu;
+  const uint32_t x2 = neg | (neg << 15);   // neg bit e at e, neg bit e at e + 15
+  uint4 u;
+  u.x = ss ^ ((x2 << 15) & 0x80008000u);
+  u.y = ss ^ ((x2 << 13) & 0x80008000u);
+  u.z = ss ^ ((x2 << 11) & 0x80008000u);
+  u.w = ss ^ ((x2 << 9) & 0x80008000u);
+  return u;
 }
 
 // Tile t of the grid, remapped so that each XCD (blocks b, b+8, ...) works
@@ -94,7 +109,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16_t (&acc)
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool SIGN1, bool OUT_F32>
+template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BK = 64;
   constexpr int LD = BK + 8;  // padded LDS row (elements): 144 B, conflict-free b128 reads
@@ -103,10 +118,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int A_PER = BM * BK / 8 / T;  // 16-byte chunks per thread
   constexpr int B_PER = BN * BK / 8 / T;
-  constexpr int S_PER = BN * 2 / T;       // 1-bit: (row, 32-column word) pairs per thread
   static_assert(A_PER >= 1 && BM * BK / 8 % T == 0, "A tile split");
-  static_assert(SIGN1 ? (S_PER >= 1 && BN * 2 % T == 0) : (B_PER >= 1 && BN * BK / 8 % T == 0),
-                "B tile split");
+  static_assert(B_PER >= 1 && BN * BK / 8 % T == 0, "B tile split");
   static_assert(EPI != 2 || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LD];
@@ -144,16 +157,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   const int kc = (tid & 7) * 8;
   const int r0 = tid >> 3;
   const uint16_t* Wd = static_cast<const uint16_t*>(g.W);
-  const uint32_t* Wb = static_cast<const uint32_t*>(g.W);
 
   uint4 a_reg[A_PER];
-  uint4 b_reg[SIGN1 ? 1 : B_PER];
-  uint32_t s_word[SIGN1 ? S_PER : 1];
-  uint16_t s_scale[SIGN1 ? S_PER : 1];
+  uint4 b_reg[B_PER];
 
   // Validity of the chunks in flight; applied when they are written to LDS so
   // the wait for the global loads falls after the MFMAs of the current tile.
-  bool a_ok[A_PER], b_ok[SIGN1 ? 1 : B_PER], s_ok[SIGN1 ? S_PER : 1];
+  bool a_ok[A_PER], b_ok[B_PER];
 
   auto load_tiles = [&](int k0) __attribute__((always_inline)) {
     const bool k_ok = k0 + kc < k_end;
@@ -165,28 +175,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
       a_reg[i] = *reinterpret_cast<const uint4*>(
           g.A + static_cast<size_t>(m < g.M ? m : g.M - 1) * g.lda + col);
     }
-    if constexpr (!SIGN1) {
 #pragma unroll
-      for (int i = 0; i < B_PER; ++i) {
-        bool ok;
-        const int n = b_row(r0 + i * (T / 8), ok);
-        b_ok[i] = ok && k_ok;
-        b_reg[i] = *reinterpret_cast<const uint4*>(
-            Wd + static_cast<size_t>(ok ? n : 0) * g.K + col);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < S_PER; ++i) {
-        const int c = tid + i * T;
-        bool ok;
-        const int n = b_row(c >> 1, ok);
-        const int k = k0 + (c & 1) * 32;
-        ok = ok && k < k_end;
-        const size_t row = static_cast<size_t>(ok ? n : 0);
-        s_ok[i] = ok;
-        s_word[i] = Wb[row * (g.K >> 5) + (ok ? (k >> 5) : 0)];
-        s_scale[i] = g.Wscale[row * (g.K >> 7) + (ok ? (k >> 7) : 0)];
-      }
+    for (int i = 0; i < B_PER; ++i) {
+      bool ok;
+      const int n = b_row(r0 + i * (T / 8), ok);
+      b_ok[i] = ok && k_ok;
+      b_reg[i] = *reinterpret_cast<const uint4*>(
+          Wd + static_cast<size_t>(ok ? n : 0) * g.K + col);
     }
   };
 
@@ -196,35 +191,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
       const int r = r0 + i * (T / 8);
       *reinterpret_cast<uint4*>(&As[buf][r * LD + kc]) = keep_if(a_reg[i], a_ok[i]);
     }
-    if constexpr (!SIGN1) {
 #pragma unroll
-      for (int i = 0; i < B_PER; ++i) {
-        const int r = r0 + i * (T / 8);
-        *reinterpret_cast<uint4*>(&Bs[buf][r * LD + kc]) = keep_if(b_reg[i], b_ok[i]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < S_PER; ++i) {
-        const int c = tid + i * T;
-        const int r = c >> 1, wd = c & 1;
-        // +scale for a set bit, -scale for a clear one, as bf16 bit patterns
-        // (negating flips the sign bit, whatever the sign of the scale)
-        const uint32_t pos = s_ok[i] ? f32_to_bf16(f16_to_f32(s_scale[i])) : 0u;
-        const uint32_t neg = s_ok[i] ? (pos ^ 0x8000u) : 0u;
-        const uint32_t w = s_word[i];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t h[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t b0 = (w >> (q * 8 + 2 * e)) & 1u;
-            const uint32_t b1 = (w >> (q * 8 + 2 * e + 1)) & 1u;
-            h[e] = (b0 ? pos : neg) | ((b1 ? pos : neg) << 16);
-          }
-          *reinterpret_cast<uint4*>(&Bs[buf][r * LD + wd * 32 + q * 8]) =
-              make_uint4(h[0], h[1], h[2], h[3]);
-        }
-      }
+    for (int i = 0; i < B_PER; ++i) {
+      const int r = r0 + i * (T / 8);
+      *reinterpret_cast<uint4*>(&Bs[buf][r * LD + kc]) = keep_if(b_reg[i], b_ok[i]);
     }
   };
 
@@ -290,7 +260,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 // row; their products land in discarded outputs.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
+template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32, bool SIGN1>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) {
   constexpr int BK = 64;
   constexpr int ROWB = BK * 2;          // 128 bytes
@@ -302,6 +272,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
   constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;  // DMA blocks per wave
   static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "DMA split");
   static_assert(EPI != 2 || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
+  constexpr int S_ITEMS = 2 * BN;       // 1-bit: (row, 32-column word) pairs per tile
+  static_assert(!SIGN1 || (S_ITEMS <= NW * 64 && S_ITEMS % 64 == 0), "1-bit items");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int wi = xcd_tile(blockIdx.x, gridDim.x);
@@ -314,38 +286,73 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lh = lane >> 5;
   const uint16_t* W = static_cast<const uint16_t*>(g.W);
+  // weight row of B-tile row r (SwiGLU: each wavefront column holds TN/2 gate
+  // rows then the TN/2 up rows of the same output columns); rows past N are
+  // clamped, their products land in discarded outputs
+  auto b_row = [&](int r) -> int {
+    if constexpr (EPI == 2) {
+      const int w = r / TN, rr = r % TN;
+      const int jj = min(nt * (BN / 2) + w * (TN / 2) + rr % (TN / 2), g.N - 1);
+      return rr >= TN / 2 ? g.up_row + jj : jj;
+    } else {
+      return min(nt * BN + r, g.N - 1);
+    }
+  };
 
   // global source rows of this lane's DMA chunks (fixed over the K loop)
   const int drow = lane >> 3, dslot = lane & 7;
   const uint16_t* a_src[A_PW];
-  const uint16_t* b_src[B_PW];
+  const uint16_t* b_src[SIGN1 ? 1 : B_PW];
 #pragma unroll
   for (int j = 0; j < A_PW; ++j) {
     const int row = (wave * A_PW + j) * 8 + drow;
     const int m = min(m0 + row, g.M - 1);
     a_src[j] = g.A + static_cast<size_t>(m) * g.lda + (dslot ^ swz8(row)) * 8;
   }
+  if constexpr (!SIGN1) {
 #pragma unroll
-  for (int j = 0; j < B_PW; ++j) {
-    const int row = (wave * B_PW + j) * 8 + drow;
-    int n;
-    if constexpr (EPI == 2) {
-      const int w = row / TN, rr = row % TN;
-      const int jj = min(nt * (BN / 2) + w * (TN / 2) + rr % (TN / 2), g.N - 1);
-      n = rr >= TN / 2 ? g.up_row + jj : jj;
-    } else {
-      n = min(nt * BN + row, g.N - 1);
+    for (int j = 0; j < B_PW; ++j) {
+      const int row = (wave * B_PW + j) * 8 + drow;
+      b_src[j] = W + static_cast<size_t>(b_row(row)) * g.K + (dslot ^ swz8(row)) * 8;
     }
-    b_src[j] = W + static_cast<size_t>(n) * g.K + (dslot ^ swz8(row)) * 8;
   }
+  // 1-bit weights: thread i < 2*BN owns (B-tile row i/2, 32-column word i%2),
+  // loads its sign word and group scale two tiles ahead and expands them into
+  // bf16 +-scale in the stage the barrier has just freed (the next barrier
+  // publishes it); ownership is wavefront-uniform
+  const bool s_own = SIGN1 && tid < S_ITEMS;
+  const int s_row = min(tid >> 1, BN - 1), s_wd = tid & 1;
+  const uint32_t* s_wsrc = nullptr;
+  const uint16_t* s_ssrc = nullptr;
+  if constexpr (SIGN1) {
+    const size_t wr = static_cast<size_t>(b_row(s_row));
+    s_wsrc = static_cast<const uint32_t*>(g.W) + wr * (g.K >> 5) + s_wd;
+    s_ssrc = g.Wscale + wr * (g.K >> 7);
+  }
+  const int s_off = A_BYTES + s_row * ROWB, s_sw = swz8(s_row);
+  auto load_s = [&](int kt, uint32_t& word, uint32_t& scale) __attribute__((always_inline)) {
+    const int k0 = k_begin + kt * BK;
+    word = s_wsrc[k0 >> 5];
+    scale = s_ssrc[k0 >> 7];
+  };
+  auto store_s = [&](int kt, uint32_t word, uint32_t scale) __attribute__((always_inline)) {
+    char* st = smem + (kt & 1) * STAGE + s_off;
+    const uint32_t sbf = f32_to_bf16(f16_to_f32(static_cast<uint16_t>(scale)));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(st + (((4 * s_wd + q) ^ s_sw) << 4)) =
+          sign1_expand8((word >> (8 * q)) & 0xffu, sbf);
+  };
 
   auto issue = [&](int kt) __attribute__((always_inline)) {
     const int k0 = k_begin + kt * BK;
     char* st = smem + (kt & 1) * STAGE;
 #pragma unroll
     for (int j = 0; j < A_PW; ++j) dma16(a_src[j] + k0, st + (wave * A_PW + j) * 1024);
+    if constexpr (!SIGN1) {
 #pragma unroll
-    for (int j = 0; j < B_PW; ++j) dma16(b_src[j] + k0, st + A_BYTES + (wave * B_PW + j) * 1024);
+      for (int j = 0; j < B_PW; ++j) dma16(b_src[j] + k0, st + A_BYTES + (wave * B_PW + j) * 1024);
+    }
   };
 
   f32x16_t acc[FM][FN];
@@ -379,10 +386,28 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
   // wait for tile kt+1, barrier (every wave has read all of tile kt), refill
   // tile kt's stage with tile kt+2, read step 0 of tile kt+1, then step 3's MFMAs.
   const int nk = (k_end - k_begin) / BK;
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 1) __builtin_amdgcn_s_waitcnt(VmWait<A_PW + B_PW>::imm);
-  else __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+  uint32_t s_word = 0, s_scale = 0;   // 1-bit: tile kt+2's item, in flight during tile kt
+  if constexpr (SIGN1) {
+    // tiles 0 and 1 are expanded before the first barrier
+    uint32_t w0 = 0, c0 = 0, w1 = 0, c1 = 0;
+    issue(0);
+    if (s_own) load_s(0, w0, c0);
+    if (nk > 1) {
+      issue(1);
+      if (s_own) load_s(1, w1, c1);
+    }
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+    if (s_own) {
+      store_s(0, w0, c0);
+      if (nk > 1) store_s(1, w1, c1);
+      if (nk > 2) load_s(2, s_word, s_scale);
+    }
+  } else {
+    issue(0);
+    if (nk > 1) issue(1);
+    if (nk > 1) __builtin_amdgcn_s_waitcnt(VmWait<A_PW + B_PW>::imm);
+    else __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+  }
   lds_barrier();
   TLP_FRAGS(af0, bf0, smem, ch[0])
   // drain every scalar load too: a scalar load still pending at the loop
@@ -404,9 +429,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
     __builtin_amdgcn_sched_barrier(0);
     TLP_MMA(af0, bf0)
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // tile kt+1, the only copy in flight
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // tile kt+1 (and tile kt+2's 1-bit item)
     lds_barrier();
-    if (kt + 2 < nk) issue(kt + 2);
+    if (kt + 2 < nk) {
+      issue(kt + 2);
+      if constexpr (SIGN1) {
+        if (s_own) {
+          store_s(kt + 2, s_word, s_scale);
+          if (kt + 3 < nk) load_s(kt + 3, s_word, s_scale);
+        }
+      }
+    }
     const char* st1 = smem + ((kt + 1) & 1) * STAGE;
     TLP_FRAGS(af0, bf0, st1, ch[0])
     __builtin_amdgcn_sched_barrier(0);
@@ -456,20 +489,6 @@ __device__ __forceinline__ int swiglu_b_row(const GemmArgs& g, int nt, int rr) {
   const int wn = rr / COLS, q = rr % COLS;
   const int idx = min(nt * COLS + wn * (COLS / 2) + 8 * (q / 16) + (q & 7), g.N - 1);
   return (q & 8) ? g.up_row + idx : idx;
-}
-
-// 8 bf16 weights from 8 sign bits (bit e -> element e; 1 -> +scale, 0 ->
-// -scale) and the bf16 bit pattern of the scale: negating flips the sign bit.
-__device__ __forceinline__ uint4 sign1_expand8(uint32_t bits8, uint32_t sbf) {
-  const uint32_t ss = sbf | (sbf << 16);
-  const uint32_t neg = ~bits8 & 0xffu;
-  const uint32_t x2 = neg | (neg << 15);   // neg bit e at e, neg bit e at e + 15
-  uint4 u;
-  u.x = ss ^ ((x2 << 15) & 0x80008000u);
-  u.y = ss ^ ((x2 << 13) & 0x80008000u);
-  u.z = ss ^ ((x2 << 11) & 0x80008000u);
-  u.w = ss ^ ((x2 << 9) & 0x80008000u);
-  return u;
 }
 
 template <int COLS, bool SIGN1>
@@ -745,8 +764,9 @@ static hipError_t run_bf16(GemmArgs g, int splits, hipStream_t s) {
   const int cols = EPI == 2 ? BN / 2 : BN;
   g.m_tiles = (g.M + BM - 1) / BM;
   g.n_tiles = (g.N + cols - 1) / cols;
-  // the direct-to-LDS kernel needs whole 64-wide K tiles
-  const bool dma = !SIGN1 && g.K % 64 == 0;
+  // the direct-to-LDS kernels need whole 64-wide K tiles (1-bit weights
+  // always have them: K % 128 == 0)
+  const bool dma = g.K % 64 == 0;
   const int kt_w = 64;
   const int k_tiles = (g.K + kt_w - 1) / kt_w;
   if (splits > k_tiles) splits = k_tiles;
@@ -757,11 +777,15 @@ static hipError_t run_bf16(GemmArgs g, int splits, hipStream_t s) {
   const int blocks = g.m_tiles * g.n_tiles * g.splits;
   if (g.splits_out) *g.splits_out = g.splits;
   if (dma) {
-    gemm_bf16_dma_kernel<BM, BN, WM, WN, EPI, OUT_F32><<<blocks, WM * WN * 64, 0, s>>>(g);
+    gemm_bf16_dma_kernel<BM, BN, WM, WN, EPI, OUT_F32, SIGN1><<<blocks, WM * WN * 64, 0, s>>>(g);
     return hipGetLastError();
   }
-  gemm_bf16_kernel<BM, BN, WM, WN, EPI, SIGN1, OUT_F32><<<blocks, WM * WN * 64, 0, s>>>(g);
-  return hipGetLastError();
+  if constexpr (SIGN1) {
+    return hipErrorInvalidValue;   // 1-bit weights always have K % 128 == 0
+  } else {
+    gemm_bf16_kernel<BM, BN, WM, WN, EPI, OUT_F32><<<blocks, WM * WN * 64, 0, s>>>(g);
+    return hipGetLastError();
+  }
 }
 
 // Tile shape per call.  Large weight matrices take 256x256 tiles; shapes with
@@ -782,7 +806,7 @@ static int big_tiles(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256
 struct PartialPlan {
   int bn, splits;
 };
-// (the narrow tiles exist for the direct-to-LDS kernel only: dense weights, K % 64 == 0)
+// (the narrow tiles exist for the direct-to-LDS kernel only: K % 64 == 0)
 static PartialPlan partial_plan(int M, int N, int K, bool narrow_ok) {
   const int k_tiles = (K + 63) / 64;
   auto clamp = [&](int sp) { return sp < 1 ? 1 : (sp > k_tiles ? k_tiles : sp); };
@@ -822,7 +846,7 @@ int gemm_partial_splits(int M, int N, int K) {
 }
 
 // Partial epilogue with 256x128 or 256x192 tiles: the direct-to-LDS kernel only.
-template <int BN, bool OUT_F32>
+template <int BN, bool OUT_F32, bool SIGN1>
 static hipError_t run_partial_narrow(GemmArgs g, int splits, hipStream_t s) {
   g.m_tiles = (g.M + 255) / 256;
   g.n_tiles = (g.N + BN - 1) / BN;
@@ -833,9 +857,9 @@ static hipError_t run_partial_narrow(GemmArgs g, int splits, hipStream_t s) {
   g.splits = (k_tiles + per - 1) / per;
   if (g.splits_out) *g.splits_out = g.splits;
   if constexpr (BN == 192)   // 4 x 2 wavefronts of 64 x 96
-    gemm_bf16_dma_kernel<256, 192, 4, 2, 4, OUT_F32><<<g.m_tiles * g.n_tiles * g.splits, 512, 0, s>>>(g);
+    gemm_bf16_dma_kernel<256, 192, 4, 2, 4, OUT_F32, SIGN1><<<g.m_tiles * g.n_tiles * g.splits, 512, 0, s>>>(g);
   else
-    gemm_bf16_dma_kernel<256, 128, 2, 4, 4, OUT_F32><<<g.m_tiles * g.n_tiles * g.splits, 512, 0, s>>>(g);
+    gemm_bf16_dma_kernel<256, 128, 2, 4, 4, OUT_F32, SIGN1><<<g.m_tiles * g.n_tiles * g.splits, 512, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -879,9 +903,9 @@ static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
   const int cols_big = EPI == 2 ? 128 : 256;
   const long tiles_big = static_cast<long>((g.M + 255) / 256) * ((g.N + cols_big - 1) / cols_big);
   if (EPI == 4) {
-    const PartialPlan p = partial_plan(g.M, g.N, g.K, !SIGN1 && g.K % 64 == 0);
-    if (p.bn == 128) return run_partial_narrow<128, OUT_F32>(g, p.splits, s);
-    if (p.bn == 192) return run_partial_narrow<192, OUT_F32>(g, p.splits, s);
+    const PartialPlan p = partial_plan(g.M, g.N, g.K, g.K % 64 == 0);
+    if (p.bn == 128) return run_partial_narrow<128, OUT_F32, SIGN1>(g, p.splits, s);
+    if (p.bn == 192) return run_partial_narrow<192, OUT_F32, SIGN1>(g, p.splits, s);
     return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, p.splits, s);
   }
   if (tiles_big >= kCUs * 3 / 4) return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, 1, s);
