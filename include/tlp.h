@@ -87,8 +87,9 @@ typedef struct {
   int32_t kv_format;    /* tlp_kv_format (0: caches in dtype) */
 } tlp_config;
 
-/* One projection weight.  Dense: data = [N][K], scales = NULL.
- * 1-bit: data = sign words, scales = fp16 group scales (see tlp_wformat). */
+/* One projection weight.  Dense: data = [N][K], scales = NULL (ignored: the
+ * format is tlp_config.wformat).  1-bit: data = sign words, scales = fp16
+ * group scales (see tlp_wformat). */
 typedef struct {
   const void* data;
   const void* scales;

@@ -139,8 +139,15 @@ def test_sign1_negative_scales():
                         wformat="sign1"), transform=_negate_some_scales)
 
 
+def test_sign1_short_batch_negative_scales():
+    # the skinny projections with 1-bit weights: 3 rows after a prefix
+    _check_layer(_small("sign1-short-negative-scales", hidden=384, inter=640, nq=4, nkv=2,
+                        head_dim=64, n_tokens=3, start=45, max_seq=64, qk_norm=True, eps=1e-6,
+                        wformat="sign1"), transform=_negate_some_scales)
+
+
 def test_sign1_decode_step():
-    # 1-bit weights keep the tiled GEMM for short micro-batches too
+    # one token: 1-bit skinny projections
     _check_layer(_small("sign1-decode", hidden=512, inter=1024, nq=4, nkv=2, n_tokens=1,
                         start=700, max_seq=768, qk_norm=True, eps=1e-6, wformat="sign1"))
 

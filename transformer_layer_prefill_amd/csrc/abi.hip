@@ -78,7 +78,7 @@ tlp_status check_config(const tlp_config* c) {
 // Whether a micro-batch of n rows takes the skinny projections (decode steps
 // and short batches with dense bf16 weights).
 bool skinny_path(const tlp_config& c, int n) {
-  return c.dtype == TLP_BF16 && c.wformat == TLP_W_DENSE && n <= tlp::kSkinnyMaxM;
+  return c.dtype == TLP_BF16 && n <= tlp::kSkinnyMaxM;
 }
 
 // fp32 elements of the PART region for any micro-batch of at most m rows
@@ -94,10 +94,10 @@ size_t part_elems(const tlp_config& c, int m) {
   auto take = [&](size_t v) { if (v > best) best = v; };
   for (int r = 1; r <= m; ++r) {
     if (skinny_path(c, r)) {
-      take(static_cast<size_t>(skinny_splits(qkv, H)) * qkv * r);
-      take(static_cast<size_t>(skinny_splits(H, qd)) * H * r);
-      take(static_cast<size_t>(skinny_splits(2 * I, H)) * 2 * I * r);
-      take(static_cast<size_t>(skinny_splits(H, I)) * H * r);
+      take(static_cast<size_t>(skinny_splits(qkv, H, c.wformat == TLP_W_SIGN1_G128)) * qkv * r);
+      take(static_cast<size_t>(skinny_splits(H, qd, c.wformat == TLP_W_SIGN1_G128)) * H * r);
+      take(static_cast<size_t>(skinny_splits(2 * I, H, c.wformat == TLP_W_SIGN1_G128)) * 2 * I * r);
+      take(static_cast<size_t>(skinny_splits(H, I, c.wformat == TLP_W_SIGN1_G128)) * H * r);
     } else {
       const int a = gemm_partial_splits(r, H, qd);
       const int b = gemm_partial_splits(r, H, I);
@@ -263,6 +263,10 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   void* v_layer = vc + layer_off;
   const bool split = act == Act::BF16;
   const bool skinny = skinny_path(c, n);
+  // the weight format comes from the config: scales of dense weights are ignored
+  auto scales_of = [&](const tlp_weight& wt) -> const void* {
+    return c.wformat == TLP_W_SIGN1_G128 ? wt.scales : nullptr;
+  };
 
   // 1. residual assembly + attention RMSNorm.  Rows that arrive in bf16 with
   // no slices to add need no fp32 copy yet: widening bf16 is exact, so the
@@ -279,13 +283,13 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   GemmCall g{};
   g.act = act;
   g.A = xn; g.lda = H;
-  g.W = w.w_qkv.data; g.Wscale = w.w_qkv.scales;
+  g.W = w.w_qkv.data; g.Wscale = scales_of(w.w_qkv);
   g.M = n; g.N = qkv_dim; g.K = H;
   int q_parts = 0;
   const size_t qkv_part_stride = static_cast<size_t>(n) * qkv_dim;
   if (skinny) {
-    q_parts = skinny_splits(qkv_dim, H);
-    TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemm_skinny(xn, H, w.w_qkv.data, n, qkv_dim, H, part,
+    q_parts = skinny_splits(qkv_dim, H, c.wformat == TLP_W_SIGN1_G128);
+    TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemm_skinny(xn, H, w.w_qkv.data, scales_of(w.w_qkv), n, qkv_dim, H, part,
                                                   qkv_dim, qkv_part_stride, q_parts, s));
   } else {
     if (split) {
@@ -312,11 +316,11 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g = GemmCall{};
   g.act = act;
   g.A = attn; g.lda = qd;
-  g.W = w.w_o.data; g.Wscale = w.w_o.scales;
+  g.W = w.w_o.data; g.Wscale = scales_of(w.w_o);
   g.M = n; g.N = H; g.K = qd;
   if (skinny) {
-    o_parts = skinny_splits(H, qd);
-    TLP_LAUNCH(TLP_K_O_GEMM, launch_gemm_skinny(attn, qd, w.w_o.data, n, H, qd, part, H,
+    o_parts = skinny_splits(H, qd, c.wformat == TLP_W_SIGN1_G128);
+    TLP_LAUNCH(TLP_K_O_GEMM, launch_gemm_skinny(attn, qd, w.w_o.data, scales_of(w.w_o), n, H, qd, part, H,
                                                 part_stride, o_parts, s));
   } else {
     if (split) {
@@ -340,13 +344,13 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g = GemmCall{};
   g.act = act;
   g.A = xn; g.lda = H;
-  g.W = w.w_gate_up.data; g.Wscale = w.w_gate_up.scales;
+  g.W = w.w_gate_up.data; g.Wscale = scales_of(w.w_gate_up);
   g.M = n; g.N = I; g.K = H;
   if (skinny) {
     // fp32 slices of [gate ; up] x_n2, then silu(gate) * up
-    const int gu_parts = skinny_splits(2 * I, H);
+    const int gu_parts = skinny_splits(2 * I, H, c.wformat == TLP_W_SIGN1_G128);
     const size_t gu_stride = static_cast<size_t>(n) * 2 * I;
-    TLP_LAUNCH(TLP_K_GATE_UP_GEMM, launch_gemm_skinny(xn, H, w.w_gate_up.data, n, 2 * I, H, part,
+    TLP_LAUNCH(TLP_K_GATE_UP_GEMM, launch_gemm_skinny(xn, H, w.w_gate_up.data, scales_of(w.w_gate_up), n, 2 * I, H, part,
                                                       2 * I, gu_stride, gu_parts, s));
     TLP_LAUNCH(TLP_K_SWIGLU, launch_swiglu_finish(part, gu_parts, gu_stride, n, I, a, s));
   } else {
@@ -358,10 +362,10 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g = GemmCall{};
   g.act = act;
   g.A = a; g.lda = I;
-  g.W = w.w_down.data; g.Wscale = w.w_down.scales;
+  g.W = w.w_down.data; g.Wscale = scales_of(w.w_down);
   g.M = n; g.N = H; g.K = I;
   if (skinny) {
-    d_parts = skinny_splits(H, I);
+    d_parts = skinny_splits(H, I, c.wformat == TLP_W_SIGN1_G128);
   } else if (split) {
     g.epi = Epi::Partial; g.out = part; g.ldo = H; g.out_f32 = true;
     g.part_stride = part_stride; g.splits_out = &d_parts;
@@ -371,7 +375,7 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
     if (out_act) g.res_out = res;   // the output also stays in the fp32 stream
   }
   if (skinny)
-    TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm_skinny(a, I, w.w_down.data, n, H, I, part, H,
+    TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm_skinny(a, I, w.w_down.data, scales_of(w.w_down), n, H, I, part, H,
                                                    part_stride, d_parts, s));
   else
     TLP_LAUNCH(TLP_K_DOWN_GEMM, launch_gemm(g, s));
@@ -561,7 +565,7 @@ tlp_status tlp_verify_tail(const tlp_config* cfg, const void* hidden, int32_t n_
   TLP_LAUNCH(TLP_K_FINAL_NORM, launch_rownorm(act, r, s));
   // LM head: fp32 logits [n_rows][vocab]
   if (act == Act::BF16 && n_rows <= kSkinnyMaxM) {
-    TLP_LAUNCH(TLP_K_LM_HEAD, launch_gemm_skinny(workspace, H, lm_head, n_rows, vocab, H, logits,
+    TLP_LAUNCH(TLP_K_LM_HEAD, launch_gemm_skinny(workspace, H, lm_head, nullptr, n_rows, vocab, H, logits,
                                                  vocab, 0, 1, s));
   } else {
     GemmCall g{};

@@ -90,6 +90,20 @@ __device__ __forceinline__ float dot2_bf16_sum(uint32_t pair, float acc) {
                                          __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
 }
 
+// 1-bit weight format: 8 bf16 weights from 8 sign bits (bit e -> element e; 1 -> +scale, 0 ->
+// -scale) and the bf16 bit pattern of the scale: negating flips the sign bit.
+__device__ __forceinline__ uint4 sign1_expand8(uint32_t bits8, uint32_t sbf) {
+  const uint32_t ss = sbf | (sbf << 16);
+  const uint32_t neg = ~bits8 & 0xffu;
+  const uint32_t x2 = neg | (neg << 15);   // neg bit e at e, neg bit e at e + 15
+  uint4 u;
+  u.x = ss ^ ((x2 << 15) & 0x80008000u);
+  u.y = ss ^ ((x2 << 13) & 0x80008000u);
+  u.z = ss ^ ((x2 << 11) & 0x80008000u);
+  u.w = ss ^ ((x2 << 9) & 0x80008000u);
+  return u;
+}
+
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 // 16-byte global -> LDS copy per lane (global_load_lds_dwordx4); `lds` must be

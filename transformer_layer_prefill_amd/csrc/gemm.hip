@@ -42,20 +42,6 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-// 8 bf16 weights from 8 sign bits (bit e -> element e; 1 -> +scale, 0 ->
-// -scale) and the bf16 bit pattern of the scale: negating flips the sign bit.
-__device__ __forceinline__ uint4 sign1_expand8(uint32_t bits8, uint32_t sbf) {
-  const uint32_t ss = sbf | (sbf << 16);
-  const uint32_t neg = ~bits8 & 0xffu;
-  const uint32_t x2 = neg | (neg << 15);   // neg bit e at e, neg bit e at e + 15
-  uint4 u;
-  u.x = ss ^ ((x2 << 15) & 0x80008000u);
-  u.y = ss ^ ((x2 << 13) & 0x80008000u);
-  u.z = ss ^ ((x2 << 11) & 0x80008000u);
-  u.w = ss ^ ((x2 << 9) & 0x80008000u);
-  return u;
-}
-
 // Tile t of the grid, remapped so that each XCD (blocks b, b+8, ...) works
 // through a contiguous run of tiles: the M-tiles that share one weight tile
 // then meet in the same L2.

@@ -60,15 +60,16 @@ hipError_t launch_gemm(const GemmCall& c, hipStream_t s);
 int gemm_partial_splits(int M, int N, int K);
 
 // ---- skinny-M projection (decode steps, verify rows) -----------------------
-// For M <= kSkinnyMaxM rows of bf16 A [M][lda] and dense bf16 W [N][K]: K is cut
-// into `splits` slices and slice s writes its fp32 product A W^T to
-// out + s * part_stride (row stride ldo); every slice is written, also an
-// empty one (zeros).  skinny_splits picks the slice count for an N x K weight.
+// For M <= kSkinnyMaxM rows of bf16 A [M][lda] and bf16 W [N][K] (Wscale null)
+// or 1-bit W (sign words u32 [N][K/32], fp16 scales Wscale [N][K/128], K % 128
+// == 0): K is cut into `splits` slices and slice s writes its fp32 product
+// A W^T to out + s * part_stride (row stride ldo); every slice is written, also
+// an empty one (zeros).  skinny_splits picks the slice count for an N x K weight.
 constexpr int kSkinnyMaxM = 32;
 constexpr int kSkinnyMaxSplits = 8;
-int skinny_splits(int N, int K);
-hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, int M, int N, int K,
-                              float* out, int ldo, size_t part_stride, int splits,
+int skinny_splits(int N, int K, bool sign1);
+hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, const void* Wscale, int M,
+                              int N, int K, float* out, int ldo, size_t part_stride, int splits,
                               hipStream_t s);
 // act[m][i] (bf16) = silu(g) * u with g, u the sums over `splits` fp32 slices of
 // the [M][2I] gate/up product (gate columns [0, I), up columns [I, 2I)).

@@ -13,6 +13,11 @@
 // lines, so the two lanes of a row consume whole lines.  The products are
 // written as fp32 split-K slices that the following row kernel sums (or the
 // SwiGLU finish below, for the fused gate/up weight).
+//
+// 1-bit weights: lane (row r, half h) loads the row's 128 sign bits and fp16
+// group scale of each 128-wide K chunk (16 + 2 bytes instead of 256) and
+// expands the 8 bits of each k-step into bf16 +-scale in registers; slices
+// are whole 128-wide groups.
 #include "common.h"
 #include "launch.h"
 
@@ -20,7 +25,8 @@ namespace tlp {
 
 struct SkinnyArgs {
   const uint16_t* A;     // [M][lda] bf16
-  const uint16_t* W;     // [N][K] bf16
+  const void* W;         // dense: [N][K] bf16; 1-bit: sign words u32 [N][K/32]
+  const uint16_t* Wscale;   // 1-bit: fp16 [N][K/128]
   float* out;            // slice s at out + s * part_stride, [M][ldo] fp32
   size_t part_stride;
   int lda, ldo;
@@ -35,6 +41,7 @@ __device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8_t zero16() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
 
+template <bool SIGN1>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   constexpr int STEPS = 8;   // 16-wide k-steps per buffer (128 of K)
   const int lane = threadIdx.x & 63;
@@ -43,7 +50,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   const int split = item % g.splits, grp = item / g.splits;
   const int lr = lane & 31, lh = lane >> 5;
   const int n = grp * 32 + lr;
-  const uint16_t* wrow = g.W + static_cast<size_t>(n < g.N ? n : g.N - 1) * g.K + 8 * lh;
+  const size_t nr = static_cast<size_t>(n < g.N ? n : g.N - 1);
+  const uint16_t* wrow = static_cast<const uint16_t*>(g.W) + nr * g.K + 8 * lh;
+  const uint32_t* brow = static_cast<const uint32_t*>(g.W) + nr * (g.K >> 5);   // 1-bit
+  const uint16_t* srow = g.Wscale + nr * (g.K >> 7);                              // 1-bit
   const bool a_ok = lr < g.M;
   const uint16_t* arow = g.A + static_cast<size_t>(a_ok ? lr : 0) * g.lda + 8 * lh;
   const int k_begin = split * g.k_split;
@@ -55,17 +65,38 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
 
   // Two register buffers of STEPS k-steps: the loads of the next 128 of K are
   // issued before the MFMAs of the current ones.
+  // (1-bit: wv[0] holds the chunk's four sign words, wv[1] its scale)
   bf16x8_t w0[STEPS], a0[STEPS], w1[STEPS], a1[STEPS];
   auto load = [&](bf16x8_t (&wv)[STEPS], bf16x8_t (&av)[STEPS], int k) __attribute__((always_inline)) {
+    if constexpr (SIGN1) {
+      wv[0] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(brow + (k >> 5)));
+      wv[1] = __builtin_bit_cast(bf16x8_t, make_uint4(srow[k >> 7], 0, 0, 0));
+    } else {
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j) wv[j] = ld16(wrow + k + 16 * j);
+      for (int j = 0; j < STEPS; ++j) wv[j] = ld16(wrow + k + 16 * j);
+    }
 #pragma unroll
     for (int j = 0; j < STEPS; ++j) av[j] = a_ok ? ld16(arow + k + 16 * j) : zero16();
   };
   auto mma = [&](const bf16x8_t (&wv)[STEPS], const bf16x8_t (&av)[STEPS]) __attribute__((always_inline)) {
+    if constexpr (SIGN1) {
+      // k-step j covers columns 16j + 8h .. +8: word j/2, bits (j%2)*16 + 8h
+      const uint4 q = __builtin_bit_cast(uint4, wv[0]);
+      const uint32_t words[4] = {q.x, q.y, q.z, q.w};
+      const uint32_t sbf =
+          f32_to_bf16(static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(
+              __builtin_bit_cast(uint4, wv[1]).x))));
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[j], av[j], acc, 0, 0, 0);
+      for (int j = 0; j < STEPS; ++j) {
+        const uint32_t bits8 = (words[j >> 1] >> ((j & 1) * 16 + 8 * lh)) & 0xffu;
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, sign1_expand8(bits8, sbf)), av[j], acc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[j], av[j], acc, 0, 0, 0);
+    }
   };
   constexpr int KB = 16 * STEPS;
   int k = k_begin;
@@ -83,6 +114,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
       mma(w1, a1);
     }
   }
+  // (1-bit slices are whole 128-wide chunks: nothing is left here)
+  if constexpr (!SIGN1) {
   for (; k + 64 <= k_end; k += 64) {
     bf16x8_t wv[4], av[4];
 #pragma unroll
@@ -99,6 +132,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
     const bf16x8_t wv = ok ? ld16(wrow + k) : zero16();
     const bf16x8_t av = ok && a_ok ? ld16(arow + k) : zero16();
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, av, acc, 0, 0, 0);
+  }
   }
 
   // lane holds output column m = lr and weight rows grp*32 + 8*(r/4) + 4*lh + r%4
@@ -119,23 +153,29 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   }
 }
 
-int skinny_splits(int N, int K) {
+int skinny_splits(int N, int K, bool sign1) {
   const int groups = (N + 31) / 32;
-  int splits = (2048 + groups - 1) / groups;   // ~8 wavefronts per CU
+  // ~8 wavefronts per CU; 1-bit weights have 16x fewer bytes per wavefront in
+  // flight, so they take as many slices as the row passes accept
+  int splits = (2048 + groups - 1) / groups;
+  if (sign1) splits = kSkinnyMaxSplits;
   if (splits > kSkinnyMaxSplits) splits = kSkinnyMaxSplits;
-  const int max_by_k = K / 256;                 // slices of at least 256
+  const int max_by_k = K / (sign1 ? 128 : 256);  // slices of at least 256 (1-bit: 128)
   if (splits > max_by_k) splits = max_by_k;
   return splits < 1 ? 1 : splits;
 }
 
-hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, int M, int N, int K,
-                              float* out, int ldo, size_t part_stride, int splits,
+hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, const void* Wscale, int M,
+                              int N, int K, float* out, int ldo, size_t part_stride, int splits,
                               hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (M > kSkinnyMaxM || splits < 1 || (K & 7) || (lda & 7)) return hipErrorInvalidValue;
+  const bool sign1 = Wscale != nullptr;
+  if (sign1 && (K & 127)) return hipErrorInvalidValue;
   SkinnyArgs g{};
   g.A = static_cast<const uint16_t*>(A);
-  g.W = static_cast<const uint16_t*>(W);
+  g.W = W;
+  g.Wscale = static_cast<const uint16_t*>(Wscale);
   g.out = out;
   g.part_stride = part_stride;
   g.lda = lda;
@@ -146,11 +186,12 @@ hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, int M, int 
   g.splits = splits;
   // slices of whole 256-wide main-loop iterations when K allows (the last
   // slice may be shorter, or empty: it then writes zeros)
-  const int gran = K >= 256 * splits ? 256 : 64;
+  const int gran = K >= 256 * splits ? 256 : (sign1 ? 128 : 64);
   g.k_split = ((K + splits - 1) / splits + gran - 1) / gran * gran;
   g.groups = (N + 31) / 32;
   const int waves = g.groups * splits;
-  gemm_skinny_kernel<<<(waves + 3) / 4, 256, 0, s>>>(g);
+  if (sign1) gemm_skinny_kernel<true><<<(waves + 3) / 4, 256, 0, s>>>(g);
+  else gemm_skinny_kernel<false><<<(waves + 3) / 4, 256, 0, s>>>(g);
   return hipGetLastError();
 }
 
