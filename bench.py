@@ -95,28 +95,40 @@ def cpu_baseline(sh, w, x, kc, vc, budget_s=20.0):
                       f"({sh.n_tokens} tokens at start {sh.start}), mean {t:.3f} s each"}
 
 
-def csrc_sha256() -> str:
-    """Hash of the HIP sources; stored traffic counters only apply to this build."""
+CSRC = os.path.join(ROOT, "transformer_layer_prefill_amd", "csrc")
+
+# the sources that define each library kernel (its own file and the shared
+# device header); stored counters of a kernel hold while these are unchanged
+KERNEL_SOURCES = {
+    "qkv_gemm": ("gemm.hip", "common.h"), "o_gemm": ("gemm.hip", "common.h"),
+    "gate_up_gemm": ("gemm.hip", "common.h"), "down_gemm": ("gemm.hip", "common.h"),
+    "attention": ("attention.hip", "common.h"),
+}
+
+
+def source_sha256() -> dict:
+    """SHA-256 of every HIP source file; stored traffic counters apply to the
+    kernels whose source files still hash the same."""
     import hashlib
-    d = os.path.join(ROOT, "transformer_layer_prefill_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        h.update(f.encode())
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+    out = {}
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            out[f] = hashlib.sha256(fh.read()).hexdigest()
+    return out
 
 
 def stored_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE passes (scaled by the copy calibration), or None when they were
-    taken on other kernel sources or are absent."""
+    taken on other sources of that kernel or are absent."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_sha256") != csrc_sha256():
+    now, then = source_sha256(), t.get("source_sha256", {})
+    files = KERNEL_SOURCES.get(kernel, tuple(now))
+    if not isinstance(then, dict) or any(now.get(f) != then.get(f) for f in files):
         return None
     for name, v in t["kernels"].items():
         if name.split(" | ")[0] == kernel:
