@@ -111,6 +111,13 @@ def test_small_layer_swiglu112_tiles():
                         n_tokens=300, start=11, max_seq=320))
 
 
+def test_max_hidden_layer():
+    # the largest hidden size the row kernels take (two 8-element chunks per
+    # thread of a 1024-thread block), ragged token count, non-zero start
+    _check_layer(_small("bf16-max-hidden", hidden=16384, inter=1024, nq=4, nkv=2, n_tokens=20,
+                        start=3, max_seq=32))
+
+
 def test_small_layer_nonzero_index():
     # layer 2 of a 3-layer cache: offsets into the cache by layer
     _check_layer(_small("bf16-layer2", n_tokens=40, start=3, max_seq=64, n_layers=3), layer=2)
