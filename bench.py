@@ -234,7 +234,10 @@ def bench_stack(args):
     cos, sin = tlp.rope_table(sh.theta, sh.head_dim, sh.max_seq)
     cosd, sind = tensors.to_device(cos, dev), tensors.to_device(sin, dev)
     mb = sh.micro_batch
-    ws = torch.empty(tlp.workspace_bytes(cfg, min(sh.n_tokens, mb)), dtype=torch.uint8, device=dev)
+    # two workspaces: consecutive micro-batches run on two streams, one layer apart
+    copies = 1 if args.no_pipeline else 2
+    ws = torch.empty(copies * tlp.workspace_bytes(cfg, min(sh.n_tokens, mb)), dtype=torch.uint8,
+                     device=dev)
     logits = torch.empty(sh.vocab, dtype=torch.float32, device=dev)
     structs = [d.struct for d in dls]
     n_buf = args.warmup + 2 * args.steps
@@ -277,7 +280,8 @@ def bench_stack(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": sh.dtype,
         "data": "synthetic",
         "config": {"workload": sh.name, "tokens": sh.n_tokens, "layers": sh.n_layers,
-                   "micro_batch": mb, "vocab": sh.vocab, "kv_cache": sh.kv_dtype,
+                   "micro_batch": mb, "micro_batches_in_flight": copies, "vocab": sh.vocab,
+                   "kv_cache": sh.kv_dtype,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "gate_up_gemm", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -300,6 +304,8 @@ def main():
                              "llama3-8b-decode", "llama3-8b-long-decode",
                              "llama3-8b-verify-tail", "llama3-8b-stack32", "tiny-f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="32-layer chunk: one workspace, so one micro-batch at a time on one stream")
     ap.add_argument("--kv-f16", action="store_true",
                     help="keep the KV cache in IEEE fp16 (the cache type of metal_full_layer.rs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,

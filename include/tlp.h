@@ -122,7 +122,8 @@ enum { TLP_WS_RES = 0, TLP_WS_XN = 1, TLP_WS_QKV = 2, TLP_WS_ATTN = 3, TLP_WS_AC
        TLP_WS_HEAD = 5, TLP_WS_PART = 6, TLP_WS_COUNT = 7 };
 
 /* Bytes of workspace a call with up to `max_tokens` tokens per micro-batch
- * needs (tlp_prefill_chunk: max_tokens = min(n_tokens, micro_batch)).
+ * needs (tlp_prefill_chunk: max_tokens = min(n_tokens, micro_batch); twice
+ * that lets it run two micro-batches at once).
  * Returns 0 for an invalid config or max_tokens <= 0. */
 size_t tlp_workspace_bytes(const tlp_config* cfg, int32_t max_tokens);
 
@@ -169,7 +170,15 @@ tlp_status tlp_prefill_layer(const tlp_config* cfg, const tlp_layer_weights* wei
  * cfg->n_layers weight structs.  If lm_head is not NULL, after the last
  * micro-batch logits[v] = sum_k lm_head[v][k] * RMSNorm(x_last; final_norm,
  * final_eps)[k] (fp32 [vocab]); lm_head is [vocab][H] in dtype, final_norm [H]
- * in dtype.  workspace >= tlp_workspace_bytes(cfg, min(n_tokens, micro_batch)).
+ * in dtype.  workspace >= W = tlp_workspace_bytes(cfg, min(n_tokens, micro_batch)).
+ * With workspace_bytes >= 2 W and more than one micro-batch, micro-batch b
+ * uses the bytes [(b % 2) W, (b % 2 + 1) W) of the workspace and the odd ones
+ * run on a second stream that the call creates (default priority,
+ * non-blocking) and releases: each layer's attention of micro-batch b waits
+ * for the K/V that micro-batch b-1 stored for that layer, so consecutive
+ * micro-batches overlap one layer apart.  The second stream starts behind the
+ * work already on `stream` and is joined back into it before the call
+ * returns, so the call's work completes in `stream`'s order either way.
  * The caller tracks the cache position: a chunk must start where the previous
  * one ended (the stateless library cannot check that). */
 tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* layers,

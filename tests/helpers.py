@@ -54,8 +54,8 @@ class GpuRun:
         self.sin = tensors.to_device(sin, device)
         self.ws = None
 
-    def workspace(self, max_tokens):
-        nbytes = self.tlp.workspace_bytes(self.cfg, max_tokens)
+    def workspace(self, max_tokens, copies=1):
+        nbytes = copies * self.tlp.workspace_bytes(self.cfg, max_tokens)
         if self.ws is None or self.ws.numel() < nbytes:
             self.ws = self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.hidden.device)
         return self.ws
@@ -67,13 +67,16 @@ class GpuRun:
                                self.vc, self.cos, self.sin, ws)
         self.torch.cuda.synchronize()
 
-    def chunk(self, n: int, start: int, mb: int, hidden=None, head=None):
+    def chunk(self, n: int, start: int, mb: int, hidden=None, head=None, pipelined=False):
+        """pipelined: pass two workspaces' worth of bytes, so consecutive
+        micro-batches alternate halves and run on two streams."""
         h = self.hidden if hidden is None else hidden
-        ws = self.workspace(min(n, mb))
-        kw = {}
+        copies = 2 if pipelined else 1
+        ws = self.workspace(min(n, mb), copies)
+        kw = dict(workspace_bytes=copies * self.tlp.workspace_bytes(self.cfg, min(n, mb)))
         if head is not None:
             fn, W, vocab, logits = head
-            kw = dict(final_norm=fn, lm_head=W, vocab=vocab, final_eps=self.shape.eps,
+            kw.update(final_norm=fn, lm_head=W, vocab=vocab, final_eps=self.shape.eps,
                       logits=logits)
         self.tlp.prefill_chunk(self.cfg, [d.struct for d in self.layers], h, n, start, mb,
                                self.kc, self.vc, self.cos, self.sin, ws, **kw)
@@ -82,9 +85,11 @@ class GpuRun:
     def host(self, t):
         return self.tensors.to_host(t)
 
-    def residual_rows(self, n):
-        """fp32 residual stream [n][H] left in the workspace by the last call."""
-        off = self.tlp.workspace_layout(self.cfg, n)[self.tlp.WS_RES]
+    def residual_rows(self, n, half=0):
+        """fp32 residual stream [n][H] left in the workspace by the last call
+        (half 1: the second workspace of a pipelined chunk)."""
+        off = half * self.tlp.workspace_bytes(self.cfg, n) + \
+            self.tlp.workspace_layout(self.cfg, n)[self.tlp.WS_RES]
         H = self.shape.hidden
         raw = self.ws[off:off + n * H * 4]
         return raw.view(self.torch.float32).reshape(n, H).cpu().numpy().astype(np.float64)

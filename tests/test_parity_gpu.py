@@ -274,34 +274,42 @@ def test_chunk_matches_oracle_and_is_chunking_invariant():
                                            head=synth.widen(W, sh.dtype), final_eps=sh.eps)
     import torch
     outs = {}
-    for mb in (sh.micro_batch, sh.n_tokens, 7, 1):
+    # (micro-batch, pipelined): two micro-batches in flight on two streams when
+    # the workspace holds two copies
+    for mb, pipe in ((sh.micro_batch, False), (sh.n_tokens, False), (7, False), (1, False),
+                     (sh.micro_batch, True), (7, True)):
         gpu = GpuRun(sh, layers, x, kc, vc)
         from transformer_layer_prefill_amd import tensors
         fn_d, W_d = tensors.to_device(fn), tensors.to_device(W)
         logits = torch.empty(sh.vocab, dtype=torch.float32, device="cuda")
-        gpu.chunk(sh.n_tokens, sh.start, mb, head=(fn_d, W_d, sh.vocab, logits))
+        log(f"[parity] chunk mb={mb} pipelined={pipe}")
+        gpu.chunk(sh.n_tokens, sh.start, mb, head=(fn_d, W_d, sh.vocab, logits), pipelined=pipe)
         g = synth.widen(gpu.host(gpu.hidden), sh.dtype)
         g_kc, g_vc = gpu.host(gpu.kc), gpu.host(gpu.vc)
         e_h = rel_err(g, ref)
         # delta of the whole stack on the last micro-batch, from the fp32 stream
         last = (sh.n_tokens - 1) // mb * mb
-        res = gpu.residual_rows(min(sh.n_tokens, mb))[:sh.n_tokens - last]
+        half = (last // mb) % 2 if pipe else 0
+        res = gpu.residual_rows(min(sh.n_tokens, mb), half)[:sh.n_tokens - last]
         x64 = synth.widen(x, sh.dtype)
         e_d = rel_err(res - x64[last:], ref[last:] - x64[last:])
         e_l = rel_err(logits.cpu().numpy(), ref_logits)
         e_k = rel_err(synth.widen(g_kc[:, :, sh.start:sh.start + sh.n_tokens], sh.kv_dtype),
                       kc64[:, :, sh.start:sh.start + sh.n_tokens])
-        log(f"[parity] chunk mb={mb}: hidden={e_h:.2e} delta={e_d:.2e} logits={e_l:.2e} "
-            f"k={e_k:.2e}")
+        log(f"[parity] chunk mb={mb} pipelined={pipe}: hidden={e_h:.2e} delta={e_d:.2e} "
+            f"logits={e_l:.2e} k={e_k:.2e}")
         for e in (e_h, e_d, e_l, e_k):
             assert e <= 2e-2
         for l in range(sh.n_layers):
             for c_in, c_gpu in ((kc, g_kc), (vc, g_vc)):
                 check_cache_slots(sh, 0, sh.n_tokens, sh.start, c_in[l:l + 1], c_gpu[l:l + 1])
-        outs[mb] = g
+        outs[(mb, pipe)] = g
+    # the two streams run the same kernels on the same rows: bit-identical
+    for mb in (sh.micro_batch, 7):
+        assert np.array_equal(outs[(mb, True)], outs[(mb, False)])
     # two GPU results, each within 2e-2 of the exact one, differ by at most twice that
-    for mb, g in outs.items():
-        assert rel_err(g, outs[sh.micro_batch]) <= 2 * 2e-2
+    for key, g in outs.items():
+        assert rel_err(g, outs[(sh.micro_batch, False)]) <= 2 * 2e-2
 
 
 @pytest.mark.timeout(900)
@@ -311,7 +319,8 @@ def test_stack32_chunked_prefill():
     The full 32-layer float64 oracle is out of reach of a test, so this checks
     (a) layer 0's K/V slots for all 4096 tokens against the oracle, (b) the
     logits against the oracle head applied to the GPU's final last row, and
-    (c) chunking invariance: micro-batches of 512 versus 1024 tokens.
+    (c) chunking invariance: micro-batches of 512 (two in flight on two
+    streams) versus 1024 tokens (one stream).
     """
     import torch
     from transformer_layer_prefill_amd import tensors
@@ -328,7 +337,8 @@ def test_stack32_chunked_prefill():
         gpu = GpuRun(sh, layers, x, kc, vc)
         fn_d, W_d = tensors.to_device(fn), tensors.to_device(W)
         logits = torch.empty(sh.vocab, dtype=torch.float32, device="cuda")
-        gpu.chunk(sh.n_tokens, sh.start, mb, head=(fn_d, W_d, sh.vocab, logits))
+        gpu.chunk(sh.n_tokens, sh.start, mb, head=(fn_d, W_d, sh.vocab, logits),
+                  pipelined=mb == 512)
         results[mb] = (synth.widen(gpu.host(gpu.hidden), sh.dtype),
                        gpu.host(gpu.kc[0]), gpu.host(gpu.vc[0]), logits.cpu().numpy())
         log(f"[parity] stack32: mb={mb} done")

@@ -241,10 +241,13 @@ struct ProfScope {
 // added.  out_act non-null: the layer's output is also rounded into out_act
 // (and *out_parts = 0); otherwise the down projection's slices are left for
 // the next layer (*out_parts = their count; the fp32 path never splits).
+// kv_done, if not null, is recorded on s once this layer's K/V slots are in
+// the cache; kv_wait, if not null, is waited for before attention reads it.
 tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer, int n,
                      int start, const void* x_in, bool x_in_f32, int in_parts, void* out_act,
                      int* out_parts, char* kc, char* vc, const float* cs, const float* sn,
-                     char* ws, const Layout& L, hipStream_t s) {
+                     char* ws, const Layout& L, hipStream_t s, hipEvent_t kv_done = nullptr,
+                     hipEvent_t kv_wait = nullptr) {
   using namespace tlp;
   const Act act = c.dtype == TLP_F32 ? Act::F32 : Act::BF16;
   const int H = c.hidden, I = c.intermediate, hd = c.head_dim;
@@ -306,6 +309,14 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
              launch_qk_rope_store(act, kv16, qkv, n, qkv_dim, part, q_parts, qkv_part_stride,
                                   w.q_norm, w.k_norm, c.qk_norm != 0, c.rms_eps, cs, sn, k_layer,
                                   v_layer, c.max_seq, start, nq, nkv, hd, s));
+  if (kv_done) {
+    const hipError_t e = hipEventRecord(kv_done, s);
+    if (e != hipSuccess) return fail(TLP_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  }
+  if (kv_wait) {
+    const hipError_t e = hipStreamWaitEvent(s, kv_wait, 0);
+    if (e != hipSuccess) return fail(TLP_ERR_HIP, "hipStreamWaitEvent: %s", hipGetErrorString(e));
+  }
   // 3e. causal GQA attention
   // (the PART region is free here: the QKV slices have been summed)
   TLP_LAUNCH(TLP_K_ATTENTION,
@@ -395,6 +406,44 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   }
   return TLP_OK;
 }
+
+// Two micro-batches of a chunk in flight: a second stream for the odd
+// micro-batches, started behind the work already on the caller's stream, and
+// per (stream parity, layer) an event recorded once that micro-batch's K/V of
+// the layer are in the cache.  The destructor joins the second stream into
+// the caller's (all of the call's work then completes in the caller's stream
+// order, also after an error) and releases the stream and the events; HIP
+// frees them once their pending work has completed.
+struct ChunkPipe {
+  hipStream_t main = nullptr, second = nullptr;
+  std::vector<hipEvent_t> ev;   // [2][n_layers], then start and end
+  int n_layers = 0;
+
+  hipError_t init(hipStream_t s, int layers) {
+    main = s;
+    n_layers = layers;
+    hipError_t e = hipStreamCreateWithFlags(&second, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      second = nullptr;
+      return e;
+    }
+    ev.assign(2 * layers + 2, nullptr);
+    for (hipEvent_t& x : ev)
+      if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ev[2 * layers], main)) != hipSuccess) return e;
+    return hipStreamWaitEvent(second, ev[2 * layers], 0);
+  }
+  hipEvent_t kv_event(int parity, int layer) const { return ev[parity * n_layers + layer]; }
+  ~ChunkPipe() {
+    if (second) {
+      hipEvent_t end = ev.empty() ? nullptr : ev.back();
+      if (end && hipEventRecord(end, second) == hipSuccess) (void)hipStreamWaitEvent(main, end, 0);
+      (void)hipStreamDestroy(second);
+    }
+    for (hipEvent_t x : ev)
+      if (x) (void)hipEventDestroy(x);
+  }
+};
 
 }  // namespace
 
@@ -487,19 +536,39 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
   char* ws = static_cast<char*>(workspace);
   const size_t row_bytes = static_cast<size_t>(cfg->hidden) * elt_size(*cfg);
   g_last_error.clear();
-  for (int off = 0; off < n_tokens; off += mb) {
-    const int m = n_tokens - off < mb ? n_tokens - off : mb;
-    char* rows = static_cast<char*>(hidden) + static_cast<size_t>(off) * row_bytes;
-    int parts = 0;
-    for (int l = 0; l < cfg->n_layers; ++l) {
-      const bool first = l == 0, last = l == cfg->n_layers - 1;
-      s = run_layer(*cfg, layers[l], l, m, start_position + off,
-                    first ? static_cast<const void*>(rows) : ws + L.off[TLP_WS_RES], !first,
-                    parts, last ? rows : nullptr, &parts, static_cast<char*>(k_cache),
-                    static_cast<char*>(v_cache), rope_cos, rope_sin, ws, L, st);
-      if (s != TLP_OK) return s;
+  // With room for two workspaces, micro-batch b uses half b % 2 and the odd
+  // micro-batches run on a second stream, each layer's attention waiting for
+  // the previous micro-batch's K/V of that layer: consecutive micro-batches
+  // overlap, one layer apart.
+  const int n_mb = (n_tokens + mb - 1) / mb;
+  const bool pipelined = n_mb > 1 && workspace_bytes / 2 >= L.total;
+  {
+    ChunkPipe pipe;
+    if (pipelined) {
+      const hipError_t e = pipe.init(st, cfg->n_layers);
+      if (e != hipSuccess)
+        return fail(TLP_ERR_HIP, "second stream for the chunk: %s", hipGetErrorString(e));
     }
-  }
+    for (int b = 0; b < n_mb; ++b) {
+      const int off = b * mb;
+      const int m = n_tokens - off < mb ? n_tokens - off : mb;
+      const int half = pipelined ? (b & 1) : 0;
+      hipStream_t sb = half ? pipe.second : st;
+      char* wsb = ws + half * L.total;
+      char* rows = static_cast<char*>(hidden) + static_cast<size_t>(off) * row_bytes;
+      int parts = 0;
+      for (int l = 0; l < cfg->n_layers; ++l) {
+        const bool first = l == 0, last = l == cfg->n_layers - 1;
+        s = run_layer(*cfg, layers[l], l, m, start_position + off,
+                      first ? static_cast<const void*>(rows) : wsb + L.off[TLP_WS_RES], !first,
+                      parts, last ? rows : nullptr, &parts, static_cast<char*>(k_cache),
+                      static_cast<char*>(v_cache), rope_cos, rope_sin, wsb, L, sb,
+                      pipelined ? pipe.kv_event(half, l) : nullptr,
+                      pipelined && b > 0 ? pipe.kv_event(half ^ 1, l) : nullptr);
+        if (s != TLP_OK) return s;
+      }
+    }
+  }   // the second stream is joined into st here
   if (lm_head) {
     hipStream_t s = st;
     const char* last_row = static_cast<char*>(hidden) + static_cast<size_t>(n_tokens - 1) * row_bytes;
