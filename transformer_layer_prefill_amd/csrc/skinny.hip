@@ -14,6 +14,12 @@
 // written as fp32 split-K slices that the following row kernel sums (or the
 // SwiGLU finish below, for the fused gate/up weight).
 //
+// One activation row (a decode step): its address is the same for every lane,
+// so each 128-wide chunk of it is fetched with scalar loads (read-only, through
+// the constant address space) instead of one 16-byte vector load per k-step,
+// and each lane selects its 8 columns.  Every lane then holds real activations
+// (only output column 0 is stored; other columns of the product are discarded).
+//
 // 1-bit weights: lane (row r, half h) loads the row's 128 sign bits and fp16
 // group scale of each 128-wide K chunk (16 + 2 bytes instead of 256) and
 // expands the 8 bits of each k-step into bf16 +-scale in registers; slices
@@ -41,11 +47,16 @@ __device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8_t zero16() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
 
-template <bool SIGN1>
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const u32x4_t const_u32x4;
+
+template <bool SIGN1, bool ONE_ROW>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   constexpr int STEPS = 8;   // 16-wide k-steps per buffer (128 of K)
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wavefront-uniform (readfirstlane lets the compiler see it): K ranges and
+  // the one-row activation addresses are scalar
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (item >= g.groups * g.splits) return;   // whole wavefronts
   const int split = item % g.splits, grp = item / g.splits;
   const int lr = lane & 31, lh = lane >> 5;
@@ -75,8 +86,19 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) wv[j] = ld16(wrow + k + 16 * j);
     }
+    if constexpr (ONE_ROW) {
+      // columns k .. k+127 of the row: 16 uniform 16-byte pieces
+      const const_u32x4* ap = (const const_u32x4*)(g.A + k);
+      u32x4_t piece[2 * STEPS];
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j) av[j] = a_ok ? ld16(arow + k + 16 * j) : zero16();
+      for (int q = 0; q < 2 * STEPS; ++q) piece[q] = ap[q];
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j)
+        av[j] = __builtin_bit_cast(bf16x8_t, lh ? piece[2 * j + 1] : piece[2 * j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j) av[j] = a_ok ? ld16(arow + k + 16 * j) : zero16();
+    }
   };
   auto mma = [&](const bf16x8_t (&wv)[STEPS], const bf16x8_t (&av)[STEPS]) __attribute__((always_inline)) {
     if constexpr (SIGN1) {
@@ -190,8 +212,14 @@ hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, const void*
   g.k_split = ((K + splits - 1) / splits + gran - 1) / gran * gran;
   g.groups = (N + 31) / 32;
   const int waves = g.groups * splits;
-  if (sign1) gemm_skinny_kernel<true><<<(waves + 3) / 4, 256, 0, s>>>(g);
-  else gemm_skinny_kernel<false><<<(waves + 3) / 4, 256, 0, s>>>(g);
+  const unsigned blocks = (waves + 3) / 4;
+  if (M == 1) {
+    if (sign1) gemm_skinny_kernel<true, true><<<blocks, 256, 0, s>>>(g);
+    else gemm_skinny_kernel<false, true><<<blocks, 256, 0, s>>>(g);
+  } else {
+    if (sign1) gemm_skinny_kernel<true, false><<<blocks, 256, 0, s>>>(g);
+    else gemm_skinny_kernel<false, false><<<blocks, 256, 0, s>>>(g);
+  }
   return hipGetLastError();
 }
 
