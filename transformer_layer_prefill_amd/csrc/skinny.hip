@@ -20,6 +20,13 @@
 // and each lane selects its 8 columns.  Every lane then holds real activations
 // (only output column 0 is stored; other columns of the product are discarded).
 //
+// Several activation rows (2..32): the four wavefronts of a block take four
+// consecutive 32-row weight groups of the same K slice, so they share the
+// activations: each 128-wide chunk of the rows is loaded once per block (one
+// 16-byte piece per thread and 16 rows) into a double-buffered LDS tile, rows
+// padded to 272 bytes so the 16 rows a read touches hit distinct banks, with
+// one barrier per chunk.
+//
 // 1-bit weights: lane (row r, half h) loads the row's 128 sign bits and fp16
 // group scale of each 128-wide K chunk (16 + 2 bytes instead of 256) and
 // expands the 8 bits of each k-step into bf16 +-scale in registers; slices
@@ -50,15 +57,33 @@ __device__ __forceinline__ bf16x8_t zero16() { return __builtin_bit_cast(bf16x8_
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const u32x4_t const_u32x4;
 
-template <bool SIGN1, bool ONE_ROW>
+// activation rows per mode: per-lane vector loads, one row through scalar
+// loads, or rows shared by the block through LDS
+enum SkinnyRows { kRowsLane = 0, kRowsOne = 1, kRowsShared = 2 };
+
+template <bool SIGN1, int ROWS>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   constexpr int STEPS = 8;   // 16-wide k-steps per buffer (128 of K)
+  constexpr bool ONE_ROW = ROWS == kRowsOne, SHARED = ROWS == kRowsShared;
+  constexpr int AST = 17;    // LDS row stride of the shared activations, in 16-byte pieces
+  __shared__ uint4 alds[SHARED ? 2 * 32 * AST : 1];
   const int lane = threadIdx.x & 63;
   // wavefront-uniform (readfirstlane lets the compiler see it): K ranges and
   // the one-row activation addresses are scalar
-  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (item >= g.groups * g.splits) return;   // whole wavefronts
-  const int split = item % g.splits, grp = item / g.splits;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int split, grp;
+  if constexpr (SHARED) {
+    // block = 4 consecutive groups of one slice; every wavefront takes part in
+    // the loads and barriers, one past the last group stores nothing
+    const int gblocks = (g.groups + 3) / 4;
+    split = blockIdx.x / gblocks;
+    grp = (blockIdx.x % gblocks) * 4 + wave;
+  } else {
+    const int item = blockIdx.x * 4 + wave;
+    if (item >= g.groups * g.splits) return;   // whole wavefronts
+    split = item % g.splits;
+    grp = item / g.splits;
+  }
   const int lr = lane & 31, lh = lane >> 5;
   const int n = grp * 32 + lr;
   const size_t nr = static_cast<size_t>(n < g.N ? n : g.N - 1);
@@ -73,12 +98,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  if constexpr (SHARED) {
+    for (int i = threadIdx.x; i < 2 * 32 * AST; i += 256) alds[i] = make_uint4(0, 0, 0, 0);
+  }
 
   // Two register buffers of STEPS k-steps: the loads of the next 128 of K are
   // issued before the MFMAs of the current ones.
   // (1-bit: wv[0] holds the chunk's four sign words, wv[1] its scale)
   bf16x8_t w0[STEPS], a0[STEPS], w1[STEPS], a1[STEPS];
-  auto load = [&](bf16x8_t (&wv)[STEPS], bf16x8_t (&av)[STEPS], int k) __attribute__((always_inline)) {
+  auto load_w = [&](bf16x8_t (&wv)[STEPS], int k) __attribute__((always_inline)) {
     if constexpr (SIGN1) {
       wv[0] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(brow + (k >> 5)));
       wv[1] = __builtin_bit_cast(bf16x8_t, make_uint4(srow[k >> 7], 0, 0, 0));
@@ -86,7 +114,18 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) wv[j] = ld16(wrow + k + 16 * j);
     }
-    if constexpr (ONE_ROW) {
+  };
+  // (activations first: a wait for them leaves the weight loads in flight)
+  auto load = [&](bf16x8_t (&wv)[STEPS], bf16x8_t (&av)[STEPS], int k) __attribute__((always_inline)) {
+    if constexpr (SHARED) {
+      // this thread's pieces of the chunk: rows t/16 and 16 + t/16, columns
+      // k + 8*(t%16) .. +8 (raw bits in av[0], av[1])
+      const int pr = threadIdx.x >> 4, pc = threadIdx.x & 15;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (pr + 16 * h < g.M)
+          av[h] = ld16(g.A + static_cast<size_t>(pr + 16 * h) * g.lda + k + 8 * pc);
+    } else if constexpr (ONE_ROW) {
       // columns k .. k+127 of the row: 16 uniform 16-byte pieces
       const const_u32x4* ap = (const const_u32x4*)(g.A + k);
       u32x4_t piece[2 * STEPS];
@@ -98,6 +137,21 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
     } else {
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) av[j] = a_ok ? ld16(arow + k + 16 * j) : zero16();
+    }
+    load_w(wv, k);
+  };
+  // shared rows: put this thread's pieces of the chunk into LDS buffer b,
+  // barrier, then read this lane's 8 fragments (row lr, columns 16j + 8h)
+  auto share = [&](bf16x8_t (&av)[STEPS], int b) __attribute__((always_inline)) {
+    if constexpr (SHARED) {
+      const int pr = threadIdx.x >> 4, pc = threadIdx.x & 15;
+      uint4* t = alds + b * 32 * AST;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (pr + 16 * h < g.M) t[(pr + 16 * h) * AST + pc] = __builtin_bit_cast(uint4, av[h]);
+      lds_barrier();
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j) av[j] = __builtin_bit_cast(bf16x8_t, t[lr * AST + 2 * j + lh]);
     }
   };
   auto mma = [&](const bf16x8_t (&wv)[STEPS], const bf16x8_t (&av)[STEPS]) __attribute__((always_inline)) {
@@ -122,17 +176,22 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   };
   constexpr int KB = 16 * STEPS;
   int k = k_begin;
+  if constexpr (SHARED) __syncthreads();   // the zeroed tile
+  // (shared rows: chunk c goes through LDS buffer c % 2; the barrier in share()
+  // also orders the reuse of a buffer two chunks later)
   if (k + KB <= k_end) {
     load(w0, a0, k);
     k += KB;
     for (;;) {
-      if (k + KB > k_end) { mma(w0, a0); break; }
+      if (k + KB > k_end) { share(a0, 0); mma(w0, a0); break; }
       load(w1, a1, k);
       k += KB;
+      share(a0, 0);
       mma(w0, a0);
-      if (k + KB > k_end) { mma(w1, a1); break; }
+      if (k + KB > k_end) { share(a1, 1); mma(w1, a1); break; }
       load(w0, a0, k);
       k += KB;
+      share(a1, 1);
       mma(w1, a1);
     }
   }
@@ -158,7 +217,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   }
 
   // lane holds output column m = lr and weight rows grp*32 + 8*(r/4) + 4*lh + r%4
-  if (!a_ok) return;
+  if (!a_ok || grp >= g.groups) return;
   float* orow = g.out + split * g.part_stride + static_cast<size_t>(lr) * g.ldo;
   const bool vec = ((g.ldo | g.part_stride) & 3) == 0;   // float4-aligned rows
 #pragma unroll
@@ -214,11 +273,12 @@ hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, const void*
   const int waves = g.groups * splits;
   const unsigned blocks = (waves + 3) / 4;
   if (M == 1) {
-    if (sign1) gemm_skinny_kernel<true, true><<<blocks, 256, 0, s>>>(g);
-    else gemm_skinny_kernel<false, true><<<blocks, 256, 0, s>>>(g);
+    if (sign1) gemm_skinny_kernel<true, kRowsOne><<<blocks, 256, 0, s>>>(g);
+    else gemm_skinny_kernel<false, kRowsOne><<<blocks, 256, 0, s>>>(g);
   } else {
-    if (sign1) gemm_skinny_kernel<true, false><<<blocks, 256, 0, s>>>(g);
-    else gemm_skinny_kernel<false, false><<<blocks, 256, 0, s>>>(g);
+    const unsigned sblocks = static_cast<unsigned>((g.groups + 3) / 4 * splits);
+    if (sign1) gemm_skinny_kernel<true, kRowsShared><<<sblocks, 256, 0, s>>>(g);
+    else gemm_skinny_kernel<false, kRowsShared><<<sblocks, 256, 0, s>>>(g);
   }
   return hipGetLastError();
 }
