@@ -57,14 +57,14 @@ __device__ __forceinline__ bf16x8_t zero16() { return __builtin_bit_cast(bf16x8_
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const u32x4_t const_u32x4;
 
-// activation rows per mode: per-lane vector loads, one row through scalar
-// loads, or rows shared by the block through LDS
-enum SkinnyRows { kRowsLane = 0, kRowsOne = 1, kRowsShared = 2 };
+// activation rows: one row through scalar loads, or 2..32 rows shared by the
+// block through LDS (the K tails past the last 128-wide chunk load per lane)
+enum SkinnyRows { kRowsOne = 1, kRowsShared = 2 };
 
 template <bool SIGN1, int ROWS>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   constexpr int STEPS = 8;   // 16-wide k-steps per buffer (128 of K)
-  constexpr bool ONE_ROW = ROWS == kRowsOne, SHARED = ROWS == kRowsShared;
+  constexpr bool SHARED = ROWS == kRowsShared;   // else one row (kRowsOne)
   constexpr int AST = 17;    // LDS row stride of the shared activations, in 16-byte pieces
   __shared__ uint4 alds[SHARED ? 2 * 32 * AST : 1];
   const int lane = threadIdx.x & 63;
@@ -125,8 +125,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
       for (int h = 0; h < 2; ++h)
         if (pr + 16 * h < g.M)
           av[h] = ld16(g.A + static_cast<size_t>(pr + 16 * h) * g.lda + k + 8 * pc);
-    } else if constexpr (ONE_ROW) {
-      // columns k .. k+127 of the row: 16 uniform 16-byte pieces
+    } else {
+      // one row: columns k .. k+127 as 16 uniform 16-byte pieces
       const const_u32x4* ap = (const const_u32x4*)(g.A + k);
       u32x4_t piece[2 * STEPS];
 #pragma unroll
@@ -134,9 +134,6 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
 #pragma unroll
       for (int j = 0; j < STEPS; ++j)
         av[j] = __builtin_bit_cast(bf16x8_t, lh ? piece[2 * j + 1] : piece[2 * j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < STEPS; ++j) av[j] = a_ok ? ld16(arow + k + 16 * j) : zero16();
     }
     load_w(wv, k);
   };
