@@ -118,6 +118,35 @@ def test_max_hidden_layer():
                         start=3, max_seq=32))
 
 
+def test_layer_graph_replay_matches_eager():
+    # the layer call enqueues kernels only (no allocation, copy, memset or
+    # synchronisation), so it can be captured into a HIP graph; every replay,
+    # with the in-place input restored eagerly in between, equals the eager call
+    import torch
+    sh = _small("bf16-graph", n_tokens=96, start=8, max_seq=128)
+    w, x, kc, vc = _inputs(sh)
+    gpu = GpuRun(sh, [w], x, kc, vc)
+    x0 = gpu.hidden.clone()
+    gpu.layer(0, sh.n_tokens, sh.start)
+    eager = gpu.host(gpu.hidden).copy()
+    eager_kc = gpu.host(gpu.kc).copy()
+    gpu.hidden.copy_(x0)
+    ws = gpu.workspace(sh.n_tokens)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gpu.tlp.prefill_layer(gpu.cfg, gpu.layers[0].struct, 0, gpu.hidden, sh.n_tokens, sh.start,
+                              gpu.kc, gpu.vc, gpu.cos, gpu.sin, ws)
+    for i in range(3):
+        gpu.hidden.copy_(x0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        log(f"[parity] graph replay {i}")
+        assert np.array_equal(gpu.host(gpu.hidden).view(np.uint16), eager.view(np.uint16))
+        assert np.array_equal(gpu.host(gpu.kc).view(np.uint16), eager_kc.view(np.uint16))
+
+
 def test_small_layer_nonzero_index():
     # layer 2 of a 3-layer cache: offsets into the cache by layer
     _check_layer(_small("bf16-layer2", n_tokens=40, start=3, max_seq=64, n_layers=3), layer=2)
