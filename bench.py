@@ -272,6 +272,31 @@ def bench_stack(args):
     for i in range(args.steps):
         step(args.warmup + args.steps + i)
     prof = tlp.profile_end()
+
+    # one chunk call captured into a HIP graph behind a copy that restores the
+    # prompt rows (so every replay does the same work), replayed K times; a
+    # captured call runs its micro-batches one at a time on the capture stream
+    graph_ms = None
+    if not args.no_graph:
+        gh = hiddens[0]
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            gh.copy_(x0)
+            tlp.prefill_chunk(cfg, structs, gh, sh.n_tokens, sh.start, mb, kcd, vcd, cosd, sind,
+                              ws, final_norm=fn, lm_head=W, vocab=sh.vocab, final_eps=sh.eps,
+                              logits=logits)
+        graph.replay()
+        torch.cuda.synchronize()
+        log(f"[bench] timing {args.steps} graph replays")
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        del graph
     kernels = {k: {"launches": n, "avg_us": round(1e3 * t / n, 3)} for k, (n, t) in prof.items() if n}
     gemm_flops, _ = layer_flops(sh, mb, 0)
     for k, f in gemm_flops.items():
@@ -296,6 +321,7 @@ def bench_stack(args):
         "cpu_baseline": None,
         "kernels": kernels,
         "wall_s_timed": round(wall, 3),
+        "ms_per_step_graph_one_stream": None if graph_ms is None else round(graph_ms, 3),
     }
     print(json.dumps(out), flush=True)
 

@@ -179,6 +179,8 @@ tlp_status tlp_prefill_layer(const tlp_config* cfg, const tlp_layer_weights* wei
  * micro-batches overlap one layer apart.  The second stream starts behind the
  * work already on `stream` and is joined back into it before the call
  * returns, so the call's work completes in `stream`'s order either way.
+ * While `stream` is being captured into a graph the micro-batches run one at
+ * a time on it (the call then only enqueues kernels, as tlp_prefill_layer).
  * The caller tracks the cache position: a chunk must start where the previous
  * one ended (the stateless library cannot check that). */
 tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* layers,

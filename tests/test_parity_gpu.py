@@ -341,6 +341,38 @@ def test_chunk_matches_oracle_and_is_chunking_invariant():
         assert rel_err(g, outs[(sh.micro_batch, False)]) <= 2 * 2e-2
 
 
+def test_chunk_graph_capture_runs_one_stream():
+    # with two workspaces the chunk driver runs two streams, but a capturing
+    # stream gets the one-stream order, so the call captures into a graph;
+    # every replay (input restored eagerly between them) equals the eager call
+    import torch
+    sh = _chunk_shape()
+    layers = [synth.layer_weights(sh, l) for l in range(sh.n_layers)]
+    x = synth.hidden_input(sh)
+    kc, vc = synth.kv_caches(sh)
+    gpu = GpuRun(sh, layers, x, kc, vc)
+    x0 = gpu.hidden.clone()
+    gpu.chunk(sh.n_tokens, sh.start, sh.micro_batch, pipelined=True)
+    eager = gpu.host(gpu.hidden).copy()
+    mb = min(sh.n_tokens, sh.micro_batch)
+    nbytes = 2 * gpu.tlp.workspace_bytes(gpu.cfg, mb)
+    ws = gpu.workspace(mb, 2)
+    gpu.hidden.copy_(x0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gpu.tlp.prefill_chunk(gpu.cfg, [d.struct for d in gpu.layers], gpu.hidden, sh.n_tokens,
+                              sh.start, sh.micro_batch, gpu.kc, gpu.vc, gpu.cos, gpu.sin, ws,
+                              workspace_bytes=nbytes)
+    for i in range(3):
+        gpu.hidden.copy_(x0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        log(f"[parity] chunk graph replay {i}")
+        assert np.array_equal(gpu.host(gpu.hidden).view(np.uint16), eager.view(np.uint16))
+
+
 @pytest.mark.timeout(900)
 def test_stack32_chunked_prefill():
     """32-layer 8B-shape stack, 4096 tokens in micro-batches of 512, LM head.

@@ -541,7 +541,14 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
   // the previous micro-batch's K/V of that layer: consecutive micro-batches
   // overlap, one layer apart.
   const int n_mb = (n_tokens + mb - 1) / mb;
-  const bool pipelined = n_mb > 1 && workspace_bytes / 2 >= L.total;
+  bool pipelined = n_mb > 1 && workspace_bytes / 2 >= L.total;
+  if (pipelined) {
+    // a stream being captured into a graph gets the one-stream order: the
+    // call then enqueues kernels on it only
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+      pipelined = false;
+  }
   {
     ChunkPipe pipe;
     if (pipelined) {
