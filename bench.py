@@ -190,6 +190,24 @@ def bench_verify_tail(args):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    # the K steps captured into a HIP graph and replayed (the tail's inputs
+    # are not overwritten, so replays repeat the same work)
+    stream_ms = ms
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                tlp.verify_tail(cfg, x, rows, g, W, V, sh.eps, logits, tokens, ws)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms = g0.elapsed_time(g1) / args.steps
+        del graph
     tlp.profile_begin()
     for _ in range(args.steps):
         step()
@@ -204,12 +222,15 @@ def bench_verify_tail(args):
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": sh.name, "rows": rows, "hidden": H, "vocab": V,
+                   "launch": "stream" if args.no_graph else "hip_graph",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "lm_head", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None, "avg_us": head_us, "bytes_per_launch": head_bytes},
         "cpu_baseline": None,
         "kernels": kernels,
+        "ms_per_step_stream": round(stream_ms, 4),
+        "value_stream": round(rows / (stream_ms * 1e-3), 1),
     }
     print(json.dumps(out), flush=True)
 
@@ -250,10 +271,13 @@ def bench_stack(args):
     hiddens = [x0.clone() for _ in range(n_buf)]
     stream = torch.cuda.current_stream(dev)
 
-    def step(i):
+    one_ws = tlp.workspace_bytes(cfg, min(sh.n_tokens, mb))
+
+    def step(i, one_stream=False):
         tlp.prefill_chunk(cfg, structs, hiddens[i], sh.n_tokens, sh.start, mb, kcd, vcd, cosd,
                           sind, ws, final_norm=fn, lm_head=W, vocab=sh.vocab, final_eps=sh.eps,
-                          logits=logits, stream=stream)
+                          logits=logits, stream=stream,
+                          workspace_bytes=one_ws if one_stream else None)
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
         step(i)
@@ -268,9 +292,11 @@ def bench_stack(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
+    # per-kernel times from a one-stream pass: with two micro-batches in flight
+    # a kernel's events would also span the other stream's kernels
     tlp.profile_begin()
     for i in range(args.steps):
-        step(args.warmup + args.steps + i)
+        step(args.warmup + args.steps + i, one_stream=True)
     prof = tlp.profile_end()
 
     # one chunk call captured into a HIP graph behind a copy that restores the
@@ -322,6 +348,7 @@ def bench_stack(args):
         "kernels": kernels,
         "wall_s_timed": round(wall, 3),
         "ms_per_step_graph_one_stream": None if graph_ms is None else round(graph_ms, 3),
+        "kernels_timed_on": "one stream (micro-batches one at a time)",
     }
     print(json.dumps(out), flush=True)
 
