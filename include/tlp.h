@@ -17,8 +17,9 @@
  *
  * Conventions for every entry point:
  *   - Every array argument is a DEVICE pointer unless marked "host".  The
- *     caller owns every buffer; the library allocates nothing and keeps no
- *     state between calls.
+ *     caller owns every buffer; the library allocates no memory and keeps no
+ *     state between calls (tlp_prefill_chunk given two workspaces creates a
+ *     stream and events for the call and releases them before returning).
  *   - Matrices are row-major.  Activations are token-major: row t of
  *     hidden [n_tokens][hidden] is token t, at absolute position
  *     start_position + t.  Projection weights are [out_features][in_features].
