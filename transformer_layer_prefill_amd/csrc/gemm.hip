@@ -797,12 +797,13 @@ static PartialPlan partial_plan(int M, int N, int K, bool narrow_ok) {
   const int k_tiles = (K + 63) / 64;
   auto clamp = [&](int sp) { return sp < 1 ? 1 : (sp > k_tiles ? k_tiles : sp); };
   // 192-column tiles when they split N exactly into a grid that, with its
-  // slices, fills the CUs with fewer slices than 256-column tiles
+  // slices (one, if the tiles alone make a wave: 2048 tokens of the 8B QKV),
+  // fills the CUs better than 256-column tiles
   if (narrow_ok && N % 192 == 0) {
     const int t192 = ((M + 255) / 256) * (N / 192);
     const int sp192 = kCUs / t192;
     const int sp256 = kCUs / big_tiles(M, N);
-    if (sp192 >= 2 && t192 * sp192 > big_tiles(M, N) * sp256)
+    if (sp192 >= 1 && t192 * sp192 > big_tiles(M, N) * sp256)
       return {192, clamp(sp192 > kMaxSplits ? kMaxSplits : sp192)};
   }
   const int narrow = ((M + 255) / 256) * ((N + 127) / 128);
