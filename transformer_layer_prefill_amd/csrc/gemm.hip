@@ -304,8 +304,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
   }
   // 1-bit weights: thread i < 2*BN owns (B-tile row i/2, 32-column word i%2),
   // loads its sign word and group scale two tiles ahead and expands them into
-  // bf16 +-scale in the stage the barrier has just freed (the next barrier
-  // publishes it); ownership is wavefront-uniform
+  // bf16 +-scale in the stage the barrier has freed, once this wavefront's
+  // MFMAs of the iteration are issued (the next barrier publishes it);
+  // ownership is wavefront-uniform
   const bool s_own = SIGN1 && tid < S_ITEMS;
   const int s_row = min(tid >> 1, BN - 1), s_wd = tid & 1;
   const uint32_t* s_wsrc = nullptr;
@@ -417,20 +418,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // tile kt+1 (and tile kt+2's 1-bit item)
     lds_barrier();
-    if (kt + 2 < nk) {
-      issue(kt + 2);
-      if constexpr (SIGN1) {
-        if (s_own) {
-          store_s(kt + 2, s_word, s_scale);
-          if (kt + 3 < nk) load_s(kt + 3, s_word, s_scale);
-        }
-      }
-    }
+    if (kt + 2 < nk) issue(kt + 2);
     const char* st1 = smem + ((kt + 1) & 1) * STAGE;
     TLP_FRAGS(af0, bf0, st1, ch[0])
     __builtin_amdgcn_sched_barrier(0);
     TLP_MMA(af1, bf1)
     __builtin_amdgcn_sched_barrier(0);
+    // 1-bit: tile kt+2's weights into that stage, after this step's MFMAs
+    // are issued (the next iteration's barrier publishes them)
+    if constexpr (SIGN1) {
+      if (s_own && kt + 2 < nk) {
+        store_s(kt + 2, s_word, s_scale);
+        if (kt + 3 < nk) load_s(kt + 3, s_word, s_scale);
+      }
+    }
   }
   {
     const char* st = smem + (kt & 1) * STAGE;
@@ -466,10 +467,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) 
 // Dense weights: both tiles are copied global -> LDS with global_load_lds_dwordx4
 // into a double buffer.  1-bit weights: the activation tile is copied the same
 // way; thread i < 4*COLS owns (weight row i/2, 32-column word i%2) of the tile,
-// loads its sign word and group scale two tiles ahead into registers and, right
-// after the barrier that frees a stage, expands them into bf16 +-scale in that
-// stage (K % 128 == 0: a 64-wide tile lies inside one scale group).  The
-// barrier of the next iteration publishes the expanded tile before its reads.
+// loads its sign word and group scale two tiles ahead into registers and,
+// once the barrier has freed a stage and this wavefront's MFMAs of the second
+// k-step are issued, expands them into bf16 +-scale in that stage (K % 128 ==
+// 0: a 64-wide tile lies inside one scale group).  The barrier of the next
+// iteration publishes the expanded tile before its reads.
 template <int COLS>
 __device__ __forceinline__ int swiglu_b_row(const GemmArgs& g, int nt, int rr) {
   const int wn = rr / COLS, q = rr % COLS;
@@ -625,20 +627,20 @@ __global__ __launch_bounds__(512) void gemm_swiglu_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
     lds_barrier();
     // every read of tile kt is done: its stage takes tile kt+2
-    if (kt + 2 < nk) {
-      issue(kt + 2);
-      if constexpr (SIGN1) {
-        if (s_own) {
-          store_s(kt + 2, s_word, s_scale);
-          if (kt + 3 < nk) load_s(kt + 3, s_word, s_scale);
-        }
-      }
-    }
+    if (kt + 2 < nk) issue(kt + 2);
     const char* st1 = smem + ((kt + 1) & 1) * STAGE;
     TLP_FRAGS16(af0, bf0, st1, ch0)
     __builtin_amdgcn_sched_barrier(0);
     TLP_MMA16(af1, bf1)
     __builtin_amdgcn_sched_barrier(0);
+    // 1-bit: tile kt+2's weights into that stage, after this step's MFMAs
+    // are issued (the next iteration's barrier publishes them)
+    if constexpr (SIGN1) {
+      if (s_own && kt + 2 < nk) {
+        store_s(kt + 2, s_word, s_scale);
+        if (kt + 3 < nk) load_s(kt + 3, s_word, s_scale);
+      }
+    }
   }
   {
     const char* st = smem + (kt & 1) * STAGE;
