@@ -26,27 +26,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
-// Element access for the two activation types (fp32 or bf16 bit patterns).
-template <typename T> struct Elt;
-template <> struct Elt<float> {
-  static __device__ __forceinline__ float ld(float v) { return v; }
-  static __device__ __forceinline__ float st(float v) { return v; }
-};
-template <> struct Elt<uint16_t> {
-  static __device__ __forceinline__ float ld(uint16_t v) { return bf16_to_f32(v); }
-  static __device__ __forceinline__ uint16_t st(float v) { return f32_to_bf16(v); }
-};
-
 // IEEE fp16 storage (KV-cache format); stores round to nearest-even.
 typedef _Float16 f16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
-template <> struct Elt<f16_t> {
-  static __device__ __forceinline__ float ld(f16_t v) { return static_cast<float>(v); }
-  static __device__ __forceinline__ f16_t st(float v) { return static_cast<f16_t>(v); }
-};
-
-template <typename T> __device__ __forceinline__ float to_f32(T v) { return Elt<T>::ld(v); }
-template <typename T> __device__ __forceinline__ T from_f32(float v) { return Elt<T>::st(v); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
