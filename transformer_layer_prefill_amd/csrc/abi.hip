@@ -76,7 +76,7 @@ tlp_status check_config(const tlp_config* c) {
 }
 
 // Whether a micro-batch of n rows takes the skinny projections (decode steps
-// and short batches with dense bf16 weights).
+// and short batches with bf16 activations, dense or 1-bit weights).
 bool skinny_path(const tlp_config& c, int n) {
   return c.dtype == TLP_BF16 && n <= tlp::kSkinnyMaxM;
 }
