@@ -341,6 +341,34 @@ def test_chunk_matches_oracle_and_is_chunking_invariant():
         assert rel_err(g, outs[(sh.micro_batch, False)]) <= 2 * 2e-2
 
 
+def test_chunk_f32_one_and_two_streams():
+    # fp32 activations through the chunk driver (residual adds in the GEMM
+    # epilogues, no split-K slices), one micro-batch at a time and two in flight
+    sh = synth.WORKLOADS["tiny-f32"].replace(name="tiny-f32-chunk", n_tokens=40, start=5,
+                                              n_layers=2, micro_batch=16)
+    layers = [synth.layer_weights(sh, l) for l in range(sh.n_layers)]
+    x = synth.hidden_input(sh)
+    kc, vc = synth.kv_caches(sh)
+    w64 = [synth.widen_layer(sh, w) for w in layers]
+    kc64, vc64 = widen_caches(sh, kc, vc)
+    ref, _ = oracle.prefill_chunk(sh, w64, synth.widen(x, sh.dtype), sh.start, sh.micro_batch,
+                                  kc64, vc64)
+    outs = {}
+    for pipe in (False, True):
+        gpu = GpuRun(sh, layers, x, kc, vc)
+        gpu.chunk(sh.n_tokens, sh.start, sh.micro_batch, pipelined=pipe)
+        g = synth.widen(gpu.host(gpu.hidden), sh.dtype)
+        e = rel_err(g, ref)
+        log(f"[parity] f32 chunk pipelined={pipe}: hidden={e:.2e}")
+        assert e <= 1e-4
+        g_kc = gpu.host(gpu.kc)
+        e_k = rel_err(synth.widen(g_kc[:, :, sh.start:sh.start + sh.n_tokens], sh.kv_dtype),
+                      kc64[:, :, sh.start:sh.start + sh.n_tokens])
+        assert e_k <= 1e-4
+        outs[pipe] = g
+    assert np.array_equal(outs[True], outs[False])
+
+
 def test_chunk_graph_capture_runs_one_stream():
     # with two workspaces the chunk driver runs two streams, but a capturing
     # stream gets the one-stream order, so the call captures into a graph;
