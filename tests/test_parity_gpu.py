@@ -369,6 +369,31 @@ def test_chunk_f32_one_and_two_streams():
     assert np.array_equal(outs[True], outs[False])
 
 
+def test_chunk_kv16_two_streams():
+    # fp16 KV cache through the chunk driver with two micro-batches in flight
+    sh = _chunk_shape().replace(name="chunk-kv16", kv="f16")
+    layers = [synth.layer_weights(sh, l) for l in range(sh.n_layers)]
+    x = synth.hidden_input(sh)
+    kc, vc = synth.kv_caches(sh)
+    w64 = [synth.widen_layer(sh, w) for w in layers]
+    kc64, vc64 = widen_caches(sh, kc, vc)
+    ref, _ = oracle.prefill_chunk(sh, w64, synth.widen(x, sh.dtype), sh.start, sh.micro_batch,
+                                  kc64, vc64)
+    gpu = GpuRun(sh, layers, x, kc, vc)
+    gpu.chunk(sh.n_tokens, sh.start, sh.micro_batch, pipelined=True)
+    g = synth.widen(gpu.host(gpu.hidden), sh.dtype)
+    s0, n = sh.start, sh.n_tokens
+    errs = {"hidden": rel_err(g, ref)}
+    for name, c_gpu, c64 in (("k", gpu.host(gpu.kc), kc64), ("v", gpu.host(gpu.vc), vc64)):
+        errs[name] = rel_err(synth.widen(c_gpu[:, :, s0:s0 + n], sh.kv_dtype), c64[:, :, s0:s0 + n])
+    log("[parity] chunk kv16 two streams: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= 2e-2, f"{k}: {v:.3e}"
+    for c_in, c_gpu in ((kc, gpu.host(gpu.kc)), (vc, gpu.host(gpu.vc))):
+        for l in range(sh.n_layers):
+            check_cache_slots(sh, 0, n, s0, c_in[l:l + 1], c_gpu[l:l + 1])
+
+
 def test_chunk_graph_capture_runs_one_stream():
     # with two workspaces the chunk driver runs two streams, but a capturing
     # stream gets the one-stream order, so the call captures into a graph;
