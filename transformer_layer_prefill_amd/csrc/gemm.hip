@@ -653,20 +653,30 @@ __global__ __launch_bounds__(512) void gemm_swiglu_kernel(GemmArgs g) {
 #undef TLP_MMA16
 
   // epilogue: lane l holds column l16 of each fragment and rows 4*lq + r;
-  // columns 0-7 are gate, 8-15 the up values of the same output columns
+  // columns 0-7 are gate, 8-15 the up values of the same output columns.
+  // Both halves of each 16-lane row finish outputs (each SiLU is evaluated
+  // once, by the lane that stores it).
   uint16_t* out = static_cast<uint16_t*>(g.out);
+  const bool lo = l16 < 8;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = acc[i][j][r];
-        const float up = __shfl_xor(v, 8, 64);
-        const int m = m0 + wm * 64 + i * 16 + 4 * lq + r;
-        const int idx = nt * COLS + wn * (COLS / 2) + 8 * j + l16;
-        if (l16 < 8 && m < g.M && idx < g.N)
-          out[static_cast<size_t>(m) * g.ldo + idx] = f32_to_bf16(silu_f32(v) * up);
+      for (int q = 0; q < 2; ++q) {
+        // rows 2q and 2q+1 of the lane's four: the low half of each 16-lane
+        // row finishes row 2q (its gate, the up value from eight lanes on),
+        // the high half row 2q+1 (its up value, the gate from eight lanes
+        // back); one rotate by eight brings each the missing value
+        const float a0 = acc[i][j][2 * q], a1 = acc[i][j][2 * q + 1];
+        const float send = lo ? a1 : a0;
+        const float got = __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0x128, 0xf, 0xf, false));
+        const float gate = lo ? a0 : got, up = lo ? got : a1;
+        const int m = m0 + wm * 64 + i * 16 + 4 * lq + 2 * q + (lo ? 0 : 1);
+        const int idx = nt * COLS + wn * (COLS / 2) + 8 * j + (l16 & 7);
+        if (m < g.M && idx < g.N)
+          out[static_cast<size_t>(m) * g.ldo + idx] = f32_to_bf16(silu_f32(gate) * up);
       }
 }
 
