@@ -133,11 +133,14 @@ def stored_traffic(workload: str, kernel: str):
     with open(path) as f:
         t = json.load(f)
     now, then = source_sha256(), t.get("source_sha256", {})
-    files = KERNEL_SOURCES.get(kernel, tuple(now))
-    if not isinstance(then, dict) or any(now.get(f) != then.get(f) for f in files):
+    if not isinstance(then, dict):
         return None
     for name, v in t["kernels"].items():
         if name.split(" | ")[0] == kernel:
+            # the files that define the kernel symbol the counters were taken on
+            files = v.get("sources") or KERNEL_SOURCES.get(kernel, tuple(now))
+            if any(now.get(f) != then.get(f) for f in files):
+                return None
             return {"bytes": round(v["fetch_bytes"] + v["write_bytes"]),
                     "fetch_bytes": round(v["fetch_bytes"]), "write_bytes": round(v["write_bytes"]),
                     "source": f"profiles/traffic_{workload}.json"}

@@ -205,3 +205,25 @@ def test_config_of_workloads():
     for shape in synth.WORKLOADS.values():
         cfg = tensors.config_of(shape)
         assert tlp.workspace_bytes(cfg, shape.micro_batch or shape.n_tokens) > 0
+
+
+def test_stored_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
+    """bench.stored_traffic reports committed counters only while the source
+    files named by the counter entry hash as they did when it was taken."""
+    import json
+    import bench
+    now = {"gemm.hip": "a", "skinny.hip": "b", "common.h": "c"}
+    entry = {"fetch_bytes": 10.0, "write_bytes": 2.0, "sources": ["skinny.hip", "common.h"]}
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "traffic_w.json").write_text(json.dumps(
+        {"source_sha256": now, "kernels": {"gate_up_gemm | sym": entry}}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_sha256", lambda: dict(now))
+    assert bench.stored_traffic("w", "gate_up_gemm")["bytes"] == 12
+    assert bench.stored_traffic("w", "down_gemm") is None
+    assert bench.stored_traffic("missing", "gate_up_gemm") is None
+    # a file the entry does not name may change; one it names may not
+    monkeypatch.setattr(bench, "source_sha256", lambda: dict(now, **{"gemm.hip": "x"}))
+    assert bench.stored_traffic("w", "gate_up_gemm")["bytes"] == 12
+    monkeypatch.setattr(bench, "source_sha256", lambda: dict(now, **{"skinny.hip": "x"}))
+    assert bench.stored_traffic("w", "gate_up_gemm") is None
