@@ -227,3 +227,14 @@ def test_stored_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
     assert bench.stored_traffic("w", "gate_up_gemm")["bytes"] == 12
     monkeypatch.setattr(bench, "source_sha256", lambda: dict(now, **{"skinny.hip": "x"}))
     assert bench.stored_traffic("w", "gate_up_gemm") is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The bench measures one GPU; asking for more ends with a message, not a run."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
