@@ -394,6 +394,36 @@ def test_chunk_kv16_two_streams():
             check_cache_slots(sh, 0, n, s0, c_in[l:l + 1], c_gpu[l:l + 1])
 
 
+def test_chunk_sign1_weights():
+    # 1-bit weights (Qwen3-style QK-norm) through the chunk driver: two
+    # micro-batches of 64 in flight, and micro-batches of 7 rows, which take
+    # the short-batch projections, one at a time
+    sh = _chunk_shape().replace(name="chunk-sign1", wformat="sign1", qk_norm=True, eps=1e-6)
+    layers = [synth.layer_weights(sh, l) for l in range(sh.n_layers)]
+    x = synth.hidden_input(sh)
+    kc, vc = synth.kv_caches(sh)
+    w64 = [synth.widen_layer(sh, w) for w in layers]
+    kc64, vc64 = widen_caches(sh, kc, vc)
+    ref, _ = oracle.prefill_chunk(sh, w64, synth.widen(x, sh.dtype), sh.start, sh.micro_batch,
+                                  kc64, vc64)
+    s0, n = sh.start, sh.n_tokens
+    for mb, pipe in ((sh.micro_batch, True), (7, False)):
+        log(f"[parity] chunk sign1 mb={mb} pipelined={pipe}")
+        gpu = GpuRun(sh, layers, x, kc, vc)
+        gpu.chunk(n, s0, mb, pipelined=pipe)
+        g = synth.widen(gpu.host(gpu.hidden), sh.dtype)
+        errs = {"hidden": rel_err(g, ref)}
+        for name, c_gpu, c64 in (("k", gpu.host(gpu.kc), kc64), ("v", gpu.host(gpu.vc), vc64)):
+            errs[name] = rel_err(synth.widen(c_gpu[:, :, s0:s0 + n], sh.kv_dtype),
+                                 c64[:, :, s0:s0 + n])
+        log(f"[parity] chunk sign1 mb={mb}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for k, v in errs.items():
+            assert v <= 2e-2, f"mb={mb} {k}: {v:.3e}"
+        for c_in, c_gpu in ((kc, gpu.host(gpu.kc)), (vc, gpu.host(gpu.vc))):
+            for l in range(sh.n_layers):
+                check_cache_slots(sh, 0, n, s0, c_in[l:l + 1], c_gpu[l:l + 1])
+
+
 def test_chunk_graph_capture_runs_one_stream():
     # with two workspaces the chunk driver runs two streams, but a capturing
     # stream gets the one-stream order, so the call captures into a graph;
