@@ -245,6 +245,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 // at one chunk hit distinct banks.  Rows past M or N are clamped to a valid
 // row; their products land in discarded outputs.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Chunk swizzle of the 16x16x32 kernel's tiles.  A 16-byte LDS read is served
+// sixteen lanes per cycle, lanes 8h..8h+7 together with 32+8h..32+8h+7; in the
+// 16x16x32 operand layout those two sets read chunks q and q^2 of the same
+// eight rows, where the 32x32x16 layout reads q and q^1.  Rows of one parity
+// (one half of the 64 banks) therefore need swizzles that stay distinct under
+// ^2 within each group of eight rows and are all distinct within sixteen:
+// {0, 1, 4, 5} for rows 0-7 of a parity, {2, 3, 6, 7} for rows 8-15.
+__device__ __forceinline__ int swz16(int r) { return ((r >> 1) & 1) | (r & 4) | ((r >> 2) & 2); }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32, bool SIGN1>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(GemmArgs g) {
@@ -506,7 +514,7 @@ __global__ __launch_bounds__(512) void gemm_swiglu_kernel(GemmArgs g) {
 #pragma unroll
   for (int j = 0; j < A_PW; ++j) {
     const int row = (wave * A_PW + j) * 8 + drow;
-    a_src[j] = g.A + static_cast<size_t>(min(m0 + row, g.M - 1)) * g.lda + (dslot ^ swz8(row)) * 8;
+    a_src[j] = g.A + static_cast<size_t>(min(m0 + row, g.M - 1)) * g.lda + (dslot ^ swz16(row)) * 8;
   }
   const uint16_t* b_src[SIGN1 ? 1 : B_PW];
   const bool has_b = wave * B_PW < B_BLK;   // wavefront-uniform
@@ -515,7 +523,7 @@ __global__ __launch_bounds__(512) void gemm_swiglu_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < B_PW; ++j) {
       const int rr = min((wave * B_PW + j) * 8 + drow, BR - 1);
-      b_src[j] = W + static_cast<size_t>(swiglu_b_row<COLS>(g, nt, rr)) * g.K + (dslot ^ swz8(rr)) * 8;
+      b_src[j] = W + static_cast<size_t>(swiglu_b_row<COLS>(g, nt, rr)) * g.K + (dslot ^ swz16(rr)) * 8;
     }
   }
   // 1-bit: this thread's (row, word) item; S_ITEMS is a multiple of 64, so
@@ -530,7 +538,7 @@ __global__ __launch_bounds__(512) void gemm_swiglu_kernel(GemmArgs g) {
     s_ssrc = g.Wscale + wr * (g.K >> 7);
   }
   const int s_off = A_BYTES + s_row * ROWB;
-  const int s_sw = swz8(s_row);
+  const int s_sw = swz16(s_row);
 
   auto issue = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BK;
@@ -567,8 +575,8 @@ __global__ __launch_bounds__(512) void gemm_swiglu_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment rows are 16-aligned, so every row this lane reads has swz8(l16)
-  const int sw = swz8(l16);
+  // fragment rows are 16-aligned, so every row this lane reads has swz16(l16)
+  const int sw = swz16(l16);
   const int a_off = (wm * 64 + l16) * ROWB, b_off = A_BYTES + (wn * COLS + l16) * ROWB;
   const int ch0 = ((0 * 4 + lq) ^ sw) << 4, ch1 = ((1 * 4 + lq) ^ sw) << 4;
   bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
