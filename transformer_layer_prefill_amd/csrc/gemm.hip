@@ -527,9 +527,20 @@ __global__ __launch_bounds__(512) void gemm_swiglu_kernel(GemmArgs g) {
     }
   }
   // 1-bit: this thread's (row, word) item; S_ITEMS is a multiple of 64, so
-  // ownership is wavefront-uniform
+  // ownership is wavefront-uniform.  A 16-byte LDS write is served eight
+  // consecutive lanes per cycle over one 128-byte bank line, so each eight
+  // lanes must write eight different chunk slots: a wavefront's 64 lanes take
+  // the two words of its 32 rows with lane bits (3, 1, 4, 2, 5) as row bits
+  // 0-4 and lane bit 0 as the word.  Lanes 8k..8k+7 then hold both words of
+  // rows r, r+2, r+8 and r+10, whose swizzles differ in bits 0 and 1 while
+  // the word flips bit 2 of the chunk: eight different slots.
+  static_assert(!SIGN1 || BR % 32 == 0, "whole wavefronts of items");
   const bool s_own = SIGN1 && tid < S_ITEMS;
-  const int s_row = min(tid >> 1, BR - 1), s_wd = tid & 1;
+  const int s_l = tid & 63;
+  const int s_row = min((tid >> 6) * 32 + (((s_l >> 3) & 1) | (s_l & 2) | ((s_l >> 2) & 4) |
+                                           ((s_l << 1) & 8) | ((s_l >> 1) & 16)),
+                        BR - 1);
+  const int s_wd = s_l & 1;
   const uint32_t* s_wsrc = nullptr;
   const uint16_t* s_ssrc = nullptr;
   if constexpr (SIGN1) {
