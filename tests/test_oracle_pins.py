@@ -287,6 +287,100 @@ def test_layer_k_slot_holds_key_roped_at_its_absolute_position():
             np.testing.assert_allclose(kc[0, j, p], expect, atol=1e-15)
 
 
+def _qkv_weights_from_vectors(q_pre, k_pre, v_pre, hidden):
+    """Fused QKV rows that map the all-ones normed row onto the given vectors:
+    every column of row d holds vec[d] / H, so the row's dot product with
+    H ones is vec[d] (exact for the dyadic values used here)."""
+    rows = [np.full(hidden, c / hidden) for vecs in (q_pre, k_pre, v_pre)
+            for head in vecs for c in head]
+    return np.array(rows, dtype=np.float64)
+
+
+@pytest.mark.parametrize("case", _golden()["qk_norm_rope"])
+def test_qk_norm_rope_hand_case(case):
+    # the query and key of one token at a known position, through the layer's
+    # own projection, per-head QK-norm and RoPE (qkv_rows), and the K/V values
+    # the layer leaves in the cache slot of that position (prefill_layer)
+    hd, nq, nkv = case["head_dim"], case["n_q_heads"], case["n_kv_heads"]
+    H = 4
+    sh = synth.Shape("qk-hand", hidden=H, inter=4, nq=nq, nkv=nkv, head_dim=hd, qk_norm=True,
+                     eps=case["eps"], theta=case["theta"], n_tokens=1, start=case["position"],
+                     max_seq=8, dtype="f32")
+    w = {"attn_norm": np.ones(H), "q_norm": np.array(case["q_gain"]),
+         "k_norm": np.array(case["k_gain"]),
+         "w_qkv": _qkv_weights_from_vectors(case["q_pre"], case["k_pre"], case["v_pre"], H),
+         "w_o": np.zeros((H, nq * hd)), "ffn_norm": np.ones(H),
+         "w_gate_up": np.zeros((2 * sh.inter, H)), "w_down": np.zeros((H, sh.inter))}
+    x = np.ones((1, H))
+    p = case["position"]
+    q, k, v = oracle.qkv_rows(sh, w, x, np.array([p]))
+    exp_q = np.array([_eval(h) for h in case["expected_q"]])
+    exp_k = np.array([_eval(h) for h in case["expected_k"]])
+    exp_v = np.array([_eval(h) for h in case["expected_v"]])
+    np.testing.assert_allclose(q[0], exp_q, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(k[0], exp_k, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(v[0], exp_v, rtol=0, atol=0)
+    kc = np.zeros((1, nkv, sh.max_seq, hd))
+    vc = np.zeros((1, nkv, sh.max_seq, hd))
+    oracle.prefill_layer(sh, w, 0, x, p, kc, vc)
+    np.testing.assert_allclose(kc[0, :, p], exp_k, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(vc[0, :, p], exp_v, rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("start", [5, 7])
+def test_layer_scores_follow_normed_roped_query(start):
+    # The query side of the layer, end to end.  The hidden row is constant, so
+    # with a unit attention gain and eps 0 the normed row is all ones.  W_q
+    # makes head 0's query e_0 and head 1's 3*e_1 before QK-norm: per head the
+    # norm gives sqrt(hd)*g_q[0]*e_0 and sqrt(hd)*g_q[1]*e_1.  The cache slots
+    # u < p hold K_u = R_u(e_0 + e_1) and one-hot V_u = e_u, so after RoPE the
+    # score of head h against slot u is g_q[h] * cos((p-u) * theta_h) (the
+    # 1/sqrt(hd) scale cancels the sqrt(hd)).  The token's own key is
+    # sqrt(hd)*g_k[2]*e_2 roped at p, orthogonal to both queries (score 0),
+    # and its value is 0.  W_o = identity and W_down = 0, so the output row is
+    # the input plus, for head h, the softmax weight of slot u on hidden dim
+    # h*hd + u.  Non-uniform gains make a swapped q/k gain, a norm taken after
+    # RoPE or over all heads at once, and an unrotated or rescaled query change
+    # the result.
+    hd, nq, nkv, H, theta = 8, 2, 1, 16, 1e4
+    p = start
+    sh = synth.Shape("q-path", hidden=H, inter=4, nq=nq, nkv=nkv, head_dim=hd, qk_norm=True,
+                     eps=0.0, theta=theta, n_tokens=1, start=p, max_seq=8, dtype="f32")
+    g_q = np.array([1.5, 0.75, 1.1, 0.9, 1.2, 0.8, 1.3, 0.7])
+    g_k = np.array([0.6, 1.4, 1.25, 0.95, 1.05, 0.85, 1.15, 0.65])
+    q_pre = [[1.0 if d == 0 else 0.0 for d in range(hd)], [3.0 if d == 1 else 0.0 for d in range(hd)]]
+    k_pre = [[1.0 if d == 2 else 0.0 for d in range(hd)]]
+    v_pre = [[0.0] * hd]
+    w = {"attn_norm": np.ones(H), "q_norm": g_q, "k_norm": g_k,
+         "w_qkv": _qkv_weights_from_vectors(q_pre, k_pre, v_pre, H),
+         "w_o": np.eye(H), "ffn_norm": np.ones(H),
+         "w_gate_up": np.zeros((2 * sh.inter, H)), "w_down": np.zeros((H, sh.inter))}
+    freq = [theta ** (-2.0 * i / hd) for i in range(hd // 2)]
+    kc = np.full((1, nkv, sh.max_seq, hd), np.nan)
+    vc = np.full((1, nkv, sh.max_seq, hd), np.nan)
+    for u in range(p):
+        kc[0, 0, u] = 0.0
+        for i in (0, 1):
+            kc[0, 0, u, i] = math.cos(u * freq[i])
+            kc[0, 0, u, i + hd // 2] = math.sin(u * freq[i])
+        vc[0, 0, u] = 0.0
+        vc[0, 0, u, u] = 1.0
+    x = np.full((1, H), 2.0)
+    out = oracle.prefill_layer(sh, w, 0, x, p, kc, vc)
+    expect = np.full(H, 2.0)
+    for h in range(nq):
+        e = [math.exp(g_q[h] * math.cos((p - u) * freq[h])) for u in range(p)]
+        den = sum(e) + 1.0                      # the token's own slot: score 0, value 0
+        for u in range(p):
+            expect[h * hd + u] += e[u] / den
+    np.testing.assert_allclose(out[0], expect, rtol=1e-14, atol=1e-14)
+    # the key written at slot p: R_p(sqrt(hd) * g_k[2] * e_2)
+    r = math.sqrt(hd) * g_k[2]
+    kp = np.zeros(hd)
+    kp[2], kp[2 + hd // 2] = r * math.cos(p * freq[2]), r * math.sin(p * freq[2])
+    np.testing.assert_allclose(kc[0, 0, p], kp, rtol=1e-14, atol=1e-14)
+
+
 def test_layer_value_path_running_mean():
     # Q = K = 0 makes every score 0, so attention is the plain mean of the visible
     # values; V head j is xn itself on its first hd dims; W_o copies head 0 back
