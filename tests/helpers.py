@@ -95,6 +95,23 @@ class GpuRun:
         return raw.view(self.torch.float32).reshape(n, H).cpu().numpy().astype(np.float64)
 
 
+def assert_act_is_rounded_stream(shape, act_rows, res_rows):
+    """The hidden rows a call returns are its fp32 residual stream rounded
+    once to the activation type: bitwise equal for fp32, and for bf16 the
+    round-to-nearest-even of each fp32 value (finite values only)."""
+    res = np.ascontiguousarray(res_rows, dtype=np.float32)
+    if shape.dtype == "f32":
+        assert np.array_equal(np.asarray(act_rows, dtype=np.float32).view(np.uint32),
+                              res.view(np.uint32))
+        return
+    u = res.view(np.uint32).astype(np.uint64)
+    rne = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    got = np.asarray(act_rows).view(np.uint16)
+    bad = np.flatnonzero(got.ravel() != rne.ravel())
+    assert bad.size == 0, (f"{bad.size} hidden values are not the RNE bf16 of the fp32 stream; "
+                           f"first at flat index {bad[0]}")
+
+
 def widen_caches(shape, kc, vc):
     return synth.widen(kc, shape.kv_dtype), synth.widen(vc, shape.kv_dtype)
 
@@ -122,3 +139,45 @@ def check_cache_slots(shape, layer, n, start, kc_in, kc_gpu):
     written = synth.widen(kc_gpu[layer, :, start:start + n], shape.kv_dtype)
     assert np.all(np.isfinite(written)), "a written cache slot holds non-finite values"
     assert np.array_equal(slot_changed, expect), "cache slots changed outside [start, start+n)"
+
+
+def split_kv_boundary_in_window(M, start, nq, nkv):
+    """Whether a split-KV key range of the attention launch begins inside the
+    query window of one wavefront, with a real query row before the boundary.
+
+    A host-side model of the library's attention launch plan (blocks of one kv
+    head and up to four query heads; four or eight wavefronts of 32 query
+    rows; key ranges of whole 64-key blocks, about 512 blocks in all when the
+    grid alone leaves CUs idle and the cache is at least twice the batch).
+    Used only to choose parity cases that cover lanes of one wavefront on both
+    sides of a range boundary; the tests never take expected values from it.
+    """
+    group = nq // nkv
+    hpb = min(group, 4)
+    quads = group // hpb
+    tiles8 = -(-M // (32 * (8 // hpb)))
+    waves = 8 if tiles8 * nkv * quads >= 256 else 4
+    bt = 32 * (waves // hpb)
+    tiles = -(-M // bt)
+    blocks = tiles * nkv * quads
+    kv_len = start + M
+    if waves != 4 or blocks >= 256 or kv_len < 2 * M:
+        return False
+    nkb = -(-kv_len // 64)
+    ns = min(-(-512 // blocks), 64, nkb // 4)
+    if ns < 2:
+        return False
+    for tile in range(tiles):
+        kv_end = start + min(M, (tile + 1) * bt)
+        nkb_t = -(-kv_end // 64)
+        per = -(-nkb_t // ns)
+        for s in range(ns):
+            lo = s * per
+            if lo >= min(nkb_t, lo + per):
+                continue
+            for sl in range(waves // hpb):
+                t0 = tile * bt + sl * 32
+                if any(start + t < lo * 64 for t in range(t0, min(t0 + 32, M))) and \
+                        start + t0 + 31 >= lo * 64:
+                    return True
+    return False

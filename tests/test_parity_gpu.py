@@ -18,8 +18,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import (GpuRun, check_cache_slots, log, oracle_layer, rel_err, tol_of,
-                     widen_caches)
+from helpers import (GpuRun, assert_act_is_rounded_stream, check_cache_slots, log,
+                     oracle_layer, rel_err, split_kv_boundary_in_window, tol_of, widen_caches)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,9 +41,11 @@ def _check_layer(shape, rows=None, layer=0, label="", transform=None):
         w = transform(w)
     gpu = GpuRun(sh, [w] * (layer + 1), x, kc, vc)
     gpu.layer(layer, sh.n_tokens, sh.start)
-    g_hidden = synth.widen(gpu.host(gpu.hidden), sh.dtype)
+    g_hidden_raw = gpu.host(gpu.hidden)
+    g_hidden = synth.widen(g_hidden_raw, sh.dtype)
     g_kc, g_vc = gpu.host(gpu.kc), gpu.host(gpu.vc)
     g_res = gpu.residual_rows(sh.n_tokens)
+    assert_act_is_rounded_stream(sh, g_hidden_raw, g_res)
     out, kc64, vc64 = oracle_layer(sh, w, layer, x, kc, vc, rows=rows)
     x64 = synth.widen(x, sh.dtype)
     sel = slice(None) if rows is None else rows
@@ -200,6 +202,22 @@ DECODE = [
            n_tokens=9, start=700, max_seq=720),
 ]
 
+# Split-KV key ranges that begin inside a wavefront's 32 query rows: the rows
+# before the boundary see no key of that range while the rows after it do
+SPLIT_STRADDLE = [
+    _small("split-straddle-9@1272", n_tokens=9, start=1272, max_seq=1344),
+    _small("split-straddle-100@1181", n_tokens=100, start=1181, max_seq=1344),
+    _small("split-straddle-g2-hd64-3@1278", hidden=256, inter=512, nq=4, nkv=2, head_dim=64,
+           n_tokens=3, start=1278, max_seq=1344),
+    _small("kv16-split-straddle-20@1261", n_tokens=20, start=1261, max_seq=1344, kv="f16"),
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_STRADDLE, ids=[s.name for s in SPLIT_STRADDLE])
+def test_split_kv_range_inside_wave(shape):
+    assert split_kv_boundary_in_window(shape.n_tokens, shape.start, shape.nq, shape.nkv)
+    _check_layer(shape)
+
 
 @pytest.mark.parametrize("shape", DECODE, ids=[s.name for s in DECODE])
 def test_decode_layer(shape):
@@ -234,8 +252,9 @@ def test_kv16_llama3_sampled():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("n,start", [(1, 4095), (16, 2000)])
+@pytest.mark.parametrize("n,start", [(1, 4095), (16, 2000), (16, 1270)])
 def test_decode_llama3(n, start):
+    # 16@1270: a split-KV key range begins at key 1280, inside the rows' window
     sh = synth.WORKLOADS["llama3-8b-layer"].replace(name=f"llama3-8b-decode-{n}@{start}",
                                                      n_tokens=n, start=start)
     _check_layer(sh)
@@ -322,6 +341,7 @@ def test_chunk_matches_oracle_and_is_chunking_invariant():
         last = (sh.n_tokens - 1) // mb * mb
         half = (last // mb) % 2 if pipe else 0
         res = gpu.residual_rows(min(sh.n_tokens, mb), half)[:sh.n_tokens - last]
+        assert_act_is_rounded_stream(sh, gpu.host(gpu.hidden)[last:], res)
         x64 = synth.widen(x, sh.dtype)
         e_d = rel_err(res - x64[last:], ref[last:] - x64[last:])
         e_l = rel_err(logits.cpu().numpy(), ref_logits)
@@ -458,8 +478,95 @@ def test_chunk_graph_capture_runs_one_stream():
         assert np.array_equal(gpu.host(gpu.hidden).view(np.uint16), eager.view(np.uint16))
 
 
+class _WidenedLayers:
+    """The float64 view of each layer's weights, made when the oracle reaches
+    that layer and dropped afterwards (32 widened 8B-shape layers would hold
+    56 GB of host memory)."""
+
+    def __init__(self, shape, layers):
+        self.shape, self.layers = shape, layers
+
+    def __len__(self):
+        return len(self.layers)
+
+    def __getitem__(self, i):
+        if i >= len(self.layers):
+            raise IndexError(i)
+        return synth.widen_layer(self.shape, self.layers[i])
+
+
+@pytest.fixture(scope="module")
+def stack32_inputs():
+    sh = synth.WORKLOADS["llama3-8b-stack32"]
+    log(f"[parity] stack32: generating {sh.n_layers} layers")
+    inputs = dict(layers=synth.stack_weights(sh, workers=16), fn=synth.final_norm(sh),
+                  W=synth.lm_head(sh, workers=16))
+    log("[parity] stack32: weights ready")
+    yield inputs
+    inputs.clear()
+
+
 @pytest.mark.timeout(900)
-def test_stack32_chunked_prefill():
+def test_stack32_against_oracle(stack32_inputs):
+    """The 32-layer 8B-shape stack end to end against the float64 oracle.
+
+    112 tokens at position 300 in micro-batches of 48 (48, 48, 16; two in
+    flight on two streams) over a cache whose slots [0, 300) hold earlier
+    keys and values, then the final norm and the 128256-entry LM head.  Every
+    hidden row, the fp32 stream of the last micro-batch, every layer's K/V
+    slots and the logits are compared at 2e-2; the K error of each layer
+    shows how the bf16 error grows with depth.
+    """
+    import torch
+    from transformer_layer_prefill_amd import tensors
+    base = synth.WORKLOADS["llama3-8b-stack32"]
+    sh = base.replace(name="llama3-8b-stack32-112@300", n_tokens=112, start=300, max_seq=512,
+                      micro_batch=48)
+    layers, fn, W = stack32_inputs["layers"], stack32_inputs["fn"], stack32_inputs["W"]
+    x = synth.hidden_input(sh)
+    kc, vc = synth.kv_caches(sh)
+    gpu = GpuRun(sh, layers, x, kc, vc)
+    fn_d, W_d = tensors.to_device(fn), tensors.to_device(W)
+    logits = torch.empty(sh.vocab, dtype=torch.float32, device="cuda")
+    gpu.chunk(sh.n_tokens, sh.start, sh.micro_batch, head=(fn_d, W_d, sh.vocab, logits),
+              pipelined=True)
+    g_raw = gpu.host(gpu.hidden)
+    g = synth.widen(g_raw, sh.dtype)
+    g_kc, g_vc = gpu.host(gpu.kc), gpu.host(gpu.vc)
+    g_logits = logits.cpu().numpy()
+    last = (sh.n_tokens - 1) // sh.micro_batch * sh.micro_batch
+    half = (last // sh.micro_batch) % 2
+    res = gpu.residual_rows(sh.micro_batch, half)[:sh.n_tokens - last]
+    del gpu
+    torch.cuda.empty_cache()
+    assert_act_is_rounded_stream(sh, g_raw[last:], res)
+    log("[parity] stack32 vs oracle: GPU done, running the float64 oracle")
+    kc64, vc64 = widen_caches(sh, kc, vc)
+    x64 = synth.widen(x, sh.dtype)
+    ref, ref_logits = oracle.prefill_chunk(sh, _WidenedLayers(sh, layers), x64, sh.start,
+                                           sh.micro_batch, kc64, vc64,
+                                           final_gain=synth.widen(fn, sh.dtype),
+                                           head=synth.widen(W, sh.dtype), final_eps=sh.eps)
+    s0, n = sh.start, sh.n_tokens
+    k_err = [rel_err(synth.widen(g_kc[l, :, s0:s0 + n], sh.kv_dtype), kc64[l, :, s0:s0 + n])
+             for l in range(sh.n_layers)]
+    v_err = [rel_err(synth.widen(g_vc[l, :, s0:s0 + n], sh.kv_dtype), vc64[l, :, s0:s0 + n])
+             for l in range(sh.n_layers)]
+    errs = {"hidden": rel_err(g, ref), "stream_last_mb": rel_err(res, ref[last:]),
+            "delta_last_mb": rel_err(res - x64[last:], ref[last:] - x64[last:]),
+            "logits": rel_err(g_logits, ref_logits), "k_max": max(k_err), "v_max": max(v_err)}
+    log("[parity] stack32 vs oracle: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    log("[parity] stack32 K error by layer: " + " ".join(f"{e:.1e}" for e in k_err))
+    log("[parity] stack32 V error by layer: " + " ".join(f"{e:.1e}" for e in v_err))
+    for k, v in errs.items():
+        assert v <= 2e-2, f"{k}: {v:.3e}"
+    for l in range(sh.n_layers):
+        for c_in, c_gpu in ((kc, g_kc), (vc, g_vc)):
+            check_cache_slots(sh, 0, n, s0, c_in[l:l + 1], c_gpu[l:l + 1])
+
+
+@pytest.mark.timeout(900)
+def test_stack32_chunked_prefill(stack32_inputs):
     """32-layer 8B-shape stack, 4096 tokens in micro-batches of 512, LM head.
 
     The full 32-layer float64 oracle is out of reach of a test, so this checks
@@ -471,13 +578,9 @@ def test_stack32_chunked_prefill():
     import torch
     from transformer_layer_prefill_amd import tensors
     sh = synth.WORKLOADS["llama3-8b-stack32"]
-    log(f"[parity] stack32: generating {sh.n_layers} layers")
-    layers = synth.stack_weights(sh, workers=16)
+    layers, fn, W = stack32_inputs["layers"], stack32_inputs["fn"], stack32_inputs["W"]
     x = synth.hidden_input(sh)
     kc, vc = synth.kv_caches(sh)
-    fn = synth.final_norm(sh)
-    W = synth.lm_head(sh, workers=16)
-    log("[parity] stack32: inputs ready")
     results = {}
     for mb in (512, 1024):
         gpu = GpuRun(sh, layers, x, kc, vc)

@@ -269,7 +269,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
     const float m_blk = mx * c;   // finite in block 0: key 0 is visible to every row
     if (__ballot(m_blk > m_run + 8.0f)) {
       const float m_new = fmaxf(m_run, m_blk);
-      const float alpha = fast_exp2(m_run - m_new);
+      // In the split form a lane whose query lies before the range's first
+      // key has seen no key yet (m_run = m_blk = -inf) while another lane of
+      // the wavefront raised the ballot: exp2(-inf - -inf) would be NaN, and
+      // its o and l (still zero) need no rescale.
+      const float alpha = SPLIT && m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
 #pragma unroll
