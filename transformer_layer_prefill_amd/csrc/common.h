@@ -96,6 +96,34 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
 #endif
 }
 
+// Buffer-resource copy global -> LDS (buffer_load_dwordx4 ... lds): a
+// wavefront-uniform descriptor (base address and byte size), a 32-bit
+// per-lane byte offset and a scalar byte offset.  Stepping along K changes
+// only the scalar offset, so a kernel keeps one 32-bit register per copy
+// stream instead of a 64-bit address.  Lane l lands at lds + 16*l; `lds` must
+// be wavefront-uniform (it becomes M0).
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ void tlp_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) uint32_t* lds,
+                                    int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p)));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r.w = 0x00020000;   // raw buffer, 32-bit data format (GFX9 descriptor word 3)
+  return r;
+}
+
+__device__ __forceinline__ void dma16_buf(i32x4_t rsrc, uint32_t voff, int soff, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  tlp_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)lds, 16,
+                      static_cast<int>(voff), soff, 0, 0);
+#endif
+}
+
 // s_waitcnt immediate that waits for vmcnt <= n and nothing else (GFX9 layout)
 template <int N>
 struct VmWait {

@@ -29,6 +29,7 @@ struct GemmArgs {
   size_t part_stride;   // Partial epilogue: elements between K-slice outputs
   int* splits_out;      // host-side only: receives the K slice count
   int up_row;  // SwiGLU: row offset of the up half (= N)
+  uint32_t a_bytes, w_bytes;   // buffer-copy kernels: bytes readable from A and from W
 };
 
 // v if ok, else zero.  Done per component: a select between two uint4
@@ -699,6 +700,400 @@ __global__ __launch_bounds__(512) void gemm_swiglu_kernel(GemmArgs g) {
       }
 }
 
+// ---- gate/up + SwiGLU, two wavefront groups half a tile apart (dense) --------
+// The block, wavefront tiles, LDS swizzle and SwiGLU epilogue are those of
+// gemm_swiglu_kernel (COLS output columns: 112 or 96).  What differs is
+// when the copies are issued.  A copy instruction holds up the wavefront that
+// issues it until the CU's load path accepts it (about 16 cycles per KB), so
+// copies issued in a burst before a run of MFMAs stall those MFMAs.  Here the
+// eight wavefronts form two groups, waves 0-3 (token rows 0-127) and 4-7
+// (rows 128-255), one wavefront of each per SIMD, that run half a K tile
+// apart; each phase ends in a workgroup barrier:
+//   phase 2kt    group 0 copies the activation tile of tile kt+1 into the
+//                stage freed by phase 2kt-1, then reads its fragments of tile
+//                kt from LDS; group 1 runs the MFMAs of tile kt-1 with the
+//                weight tile of tile kt+1 copied between them (one copy
+//                instruction every four MFMAs of the second k-step);
+//   phase 2kt+1  group 0 runs the MFMAs of tile kt; group 1 reads tile kt.
+// So the MFMA pipe of each SIMD is fed by one group while the other reads.
+// Every wavefront waits for its copies of tile kt+1 before the barrier that
+// ends phase 2kt+1.  Group 1's copies past the last tile re-copy the last
+// tile's weights into a stage nobody reads any more (a branch around them
+// would split the scheduled MFMA block); all copies are waited for before the
+// epilogue.
+template <int N> struct IntC { static constexpr int value = N; };
+
+template <int COLS>
+__global__ __launch_bounds__(512) void gemm_swiglu_pp_kernel(GemmArgs g) {
+  constexpr int BM = 256, BR = 2 * COLS, BK = 64, ROWB = 128;
+  constexpr int FM = 4, FN = COLS / 16;                     // 16x16 fragments per wavefront
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BR * ROWB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_PW = A_BYTES / 1024 / 4;                  // 8 activation blocks per group-0 wavefront
+  constexpr int B_PW = B_BYTES / 1024 / 4;                  // 8, 7 or 6 weight blocks per group-1 wavefront
+  static_assert(COLS % 16 == 0 && B_BYTES % 4096 == 0 && 4 * B_PW <= FM * FN, "tile shape");
+  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int wi = xcd_tile(blockIdx.x, gridDim.x);
+  const int mt = wi % g.m_tiles, nt = wi / g.m_tiles;
+  const int m0 = mt * BM;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, cw = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int nk = g.K / BK;
+
+  // Copy streams: a 1 KB block is 8 rows of 128 bytes; lane l fetches chunk
+  // (l & 7) ^ swz16(row) of row l >> 3.  Group-0 wavefront cw copies
+  // activation blocks 8cw .. 8cw+7, group-1 wavefront cw weight blocks
+  // B_PW*cw .. (32-bit byte offsets from the matrix bases).
+  const int drow = lane >> 3, dslot = lane & 7;
+  constexpr int C_PW = A_PW > B_PW ? A_PW : B_PW;
+  uint32_t c_src[C_PW];
+#pragma unroll
+  for (int j = 0; j < C_PW; ++j) {
+    if (grp == 0) {
+      const int row = (cw * A_PW + j) * 8 + drow;
+      c_src[j] = (static_cast<uint32_t>(min(m0 + row, g.M - 1)) * g.lda + (dslot ^ swz16(row)) * 8) * 2;
+    } else {
+      const int rr = min((cw * B_PW + j) * 8 + drow, BR - 1);
+      c_src[j] = (static_cast<uint32_t>(swiglu_b_row<COLS>(g, nt, rr)) * g.K + (dslot ^ swz16(rr)) * 8) * 2;
+    }
+  }
+  const i32x4_t c_rsrc = grp == 0 ? buffer_rsrc(g.A, g.a_bytes) : buffer_rsrc(g.W, g.w_bytes);
+  const int c_lds = grp == 0 ? cw * A_PW * 1024 : A_BYTES + cw * B_PW * 1024;
+  auto kbyte = [&](int kt) { return __builtin_amdgcn_readfirstlane(kt * BK * 2); };
+  auto copy = [&](int kt, char* st, int j) __attribute__((always_inline)) {
+    dma16_buf(c_rsrc, c_src[j], kbyte(kt), st + c_lds + j * 1024);
+  };
+  auto copy_tile = [&](int kt, char* st) __attribute__((always_inline)) {
+    if (grp == 0) {
+#pragma unroll
+      for (int j = 0; j < A_PW; ++j) copy(kt, st, j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < B_PW; ++j) copy(kt, st, j);
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment rows are 16-aligned, so every row this lane reads has swz16(l16)
+  const int sw = swz16(l16);
+  const int a_off = (wm * 64 + l16) * ROWB, b_off = A_BYTES + (wn * COLS + l16) * ROWB;
+  const int ch0 = ((0 * 4 + lq) ^ sw) << 4, ch1 = ((1 * 4 + lq) ^ sw) << 4;
+  bf16x8_t af[2][FM], bf[2][FN];
+  auto read_frags = [&](const char* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      af[0][i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 16 * ROWB + ch0);
+      af[1][i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 16 * ROWB + ch1);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      bf[0][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 16 * ROWB + ch0);
+      bf[1][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 16 * ROWB + ch1);
+    }
+  };
+  auto mfma_step = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bf[ks][j], acc[i][j], 0, 0, 0);
+  };
+  // group 1: the tile's MFMAs with the weight copies of tile ktc issued between
+  // those of the second k-step (masks: 0x8 MFMA, 0x20 vector memory read)
+  auto mfma_copy = [&](int ktc, char* st) __attribute__((always_inline)) {
+    mfma_step(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < B_PW; ++j) copy(ktc, st, j);
+    mfma_step(1);
+#pragma unroll
+    for (int j = 0; j < B_PW; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 4 * B_PW, 0);
+  };
+  auto bar = []() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
+
+  // prologue: tiles 0 and 1 in flight, each group its own part; wait for tile 0
+  copy_tile(0, smem);
+  if (nk > 1) {
+    copy_tile(1, smem + STAGE);
+    if (grp == 0) __builtin_amdgcn_s_waitcnt(VmWait<A_PW>::imm);
+    else __builtin_amdgcn_s_waitcnt(VmWait<B_PW>::imm);
+  } else {
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+  }
+  lds_barrier();
+
+  // stage P holds the tiles of parity P; the loops run two tiles per
+  // iteration so that every stage address is a constant offset
+  if (grp == 0) {
+    auto step = [&](int kt, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      // phase 2kt: activations of tile kt+1 (its stage was freed by phase
+      // 2kt-1; tile 1 came with the prologue), then the fragments of tile kt
+      if (kt >= 1 && kt + 1 < nk) copy_tile(kt + 1, smem + (P ^ 1) * STAGE);
+      read_frags(smem + P * STAGE);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 2kt+1: the MFMAs of tile kt
+      mfma_step(0);
+      mfma_step(1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wavefront's copies of tile kt+1
+      bar();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, IntC<0>{});
+      step(kt + 1, IntC<1>{});
+    }
+    if (kt < nk) step(kt, IntC<0>{});
+  } else {
+    lds_barrier();   // phase 0: group 0 reads tile 0
+    auto step = [&](int kt, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      // phase 2kt+1: the fragments of tile kt; this wavefront's weight copies
+      // of tile kt+1 must have landed before the barrier
+      read_frags(smem + P * STAGE);
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 2kt+2: the MFMAs of tile kt, with the weights of tile kt+2
+      // copied into tile kt's stage between them
+      mfma_copy(min(kt + 2, nk - 1), smem + P * STAGE);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) bar();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, IntC<0>{});
+      step(kt + 1, IntC<1>{});
+    }
+    if (kt < nk) step(kt, IntC<0>{});
+  }
+  __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // no copy may land after the block ends
+
+  // epilogue (as in gemm_swiglu_kernel): the low half of each 16-lane row
+  // finishes row 2q, the high half row 2q+1; a rotate by eight lanes brings
+  // each the value it is missing
+  uint16_t* out = static_cast<uint16_t*>(g.out);
+  const bool lo = l16 < 8;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float a0 = acc[i][j][2 * q], a1 = acc[i][j][2 * q + 1];
+        const float send = lo ? a1 : a0;
+        const float got = __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0x128, 0xf, 0xf, false));
+        const float gate = lo ? a0 : got, up = lo ? got : a1;
+        const int m = m0 + wm * 64 + i * 16 + 4 * lq + 2 * q + (lo ? 0 : 1);
+        const int idx = nt * COLS + wn * (COLS / 2) + 8 * j + (l16 & 7);
+        if (m < g.M && idx < g.N)
+          out[static_cast<size_t>(m) * g.ldo + idx] = f32_to_bf16(silu_f32(gate) * up);
+      }
+}
+
+// ---- dense projections, two wavefront groups half a tile apart ---------------
+// For 128- and 192-wide weight tiles (a 256-wide tile's accumulators and
+// fragments of a whole K tile do not fit in the registers of two wavefronts
+// per SIMD).  The tiles (256 token rows x BN weight rows, 64-wide K tiles, eight
+// wavefronts of 32x32x16 MFMAs), swizzle, K slices and epilogues of
+// gemm_bf16_dma_kernel with the copy schedule of gemm_swiglu_pp_kernel:
+// waves 0-3 (token rows 0-127) copy the activation tile at the start of
+// their read phases, waves 4-7 (rows 128-255) copy the weight tile between
+// the MFMAs of the second half of their tile.
+template <int BN, int WM, int WN, int EPI, bool OUT_F32>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_pp_dma_kernel(GemmArgs g) {
+  constexpr int BM = 256, BK = 64, ROWB = BK * 2;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_PW = A_BYTES / 1024 / 4, B_PW = B_BYTES / 1024 / 4;
+  constexpr int HALF = 2 * FM * FN;                         // MFMAs of two k-steps
+  static_assert(WM * WN == 8 && TM * 2 * (WM / 2) == BM, "waves 0-3 cover token rows 0-127");
+  static_assert(B_BYTES % 4096 == 0 && B_PW <= HALF, "copy split");
+  static_assert(EPI != 2 || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int wi = xcd_tile(blockIdx.x, gridDim.x);
+  const int split = wi % g.splits, t = wi / g.splits;
+  const int mt = t % g.m_tiles, nt = t / g.m_tiles;
+  const int m0 = mt * BM;
+  const int k_begin = split * g.k_split;
+  const int k_end = min(g.K, k_begin + g.k_split);
+  const int nk = (k_end - k_begin) / BK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, cw = wave & 3;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 31, lh = lane >> 5;
+  // weight row of B-tile row r (SwiGLU: each wavefront column holds TN/2 gate
+  // rows then the TN/2 up rows of the same output columns); rows past N are
+  // clamped, their products land in discarded outputs
+  auto b_row = [&](int r) -> int {
+    if constexpr (EPI == 2) {
+      const int w = r / TN, rr = r % TN;
+      const int jj = min(nt * (BN / 2) + w * (TN / 2) + rr % (TN / 2), g.N - 1);
+      return rr >= TN / 2 ? g.up_row + jj : jj;
+    } else {
+      return min(nt * BN + r, g.N - 1);
+    }
+  };
+
+  const int drow = lane >> 3, dslot = lane & 7;
+  constexpr int C_PW = A_PW > B_PW ? A_PW : B_PW;
+  uint32_t c_src[C_PW];
+#pragma unroll
+  for (int j = 0; j < C_PW; ++j) {
+    if (grp == 0) {
+      const int row = (cw * A_PW + j) * 8 + drow;
+      c_src[j] = (static_cast<uint32_t>(min(m0 + row, g.M - 1)) * g.lda + (dslot ^ swz8(row)) * 8) * 2;
+    } else {
+      const int row = min((cw * B_PW + j) * 8 + drow, BN - 1);
+      c_src[j] = (static_cast<uint32_t>(b_row(row)) * g.K + (dslot ^ swz8(row)) * 8) * 2;
+    }
+  }
+  const i32x4_t c_rsrc = grp == 0 ? buffer_rsrc(g.A, g.a_bytes) : buffer_rsrc(g.W, g.w_bytes);
+  const int c_lds = grp == 0 ? cw * A_PW * 1024 : A_BYTES + cw * B_PW * 1024;
+  auto kbyte = [&](int kt) { return __builtin_amdgcn_readfirstlane((k_begin + kt * BK) * 2); };
+  auto copy = [&](int kt, char* st, int j) __attribute__((always_inline)) {
+    dma16_buf(c_rsrc, c_src[j], kbyte(kt), st + c_lds + j * 1024);
+  };
+  auto copy_tile = [&](int kt, char* st) __attribute__((always_inline)) {
+    if (grp == 0) {
+#pragma unroll
+      for (int j = 0; j < A_PW; ++j) copy(kt, st, j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < B_PW; ++j) copy(kt, st, j);
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fragment rows are 32-aligned, so swz8(row) = swz8(lr)
+  const int sw = swz8(lr);
+  const int a_off = (wm * TM + lr) * ROWB, b_off = A_BYTES + (wn * TN + lr) * ROWB;
+  bf16x8_t af[4][FM], bf[4][FN];
+  auto read_frags = [&](const char* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ch = ((kk * 2 + lh) ^ sw) << 4;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[kk][i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 32 * ROWB + ch);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bf[kk][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * ROWB + ch);
+    }
+  };
+  auto mfma_steps = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = k0; kk < k0 + 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bf[kk][j], acc[i][j], 0, 0, 0);
+  };
+  // group 1: the weight copies of tile ktc spread over the MFMAs of k-steps
+  // 2 and 3 (masks: 0x8 MFMA, 0x20 vector memory read)
+  auto mfma_copy = [&](int ktc, char* st) __attribute__((always_inline)) {
+    mfma_steps(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < B_PW; ++j) copy(ktc, st, j);
+    mfma_steps(2);
+    constexpr int EVERY = HALF / B_PW;
+#pragma unroll
+    for (int j = 0; j < B_PW; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, EVERY, 0);
+    }
+    if constexpr (HALF - EVERY * B_PW > 0)
+      __builtin_amdgcn_sched_group_barrier(0x008, HALF - EVERY * B_PW, 0);
+  };
+  auto bar = []() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
+
+  copy_tile(0, smem);
+  if (nk > 1) {
+    copy_tile(1, smem + STAGE);
+    if (grp == 0) __builtin_amdgcn_s_waitcnt(VmWait<A_PW>::imm);
+    else __builtin_amdgcn_s_waitcnt(VmWait<B_PW>::imm);
+  } else {
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+  }
+  lds_barrier();
+
+  if (grp == 0) {
+    auto step = [&](int kt, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      if (kt >= 1 && kt + 1 < nk) copy_tile(kt + 1, smem + (P ^ 1) * STAGE);
+      read_frags(smem + P * STAGE);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_steps(0);
+      mfma_steps(2);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+      bar();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, IntC<0>{});
+      step(kt + 1, IntC<1>{});
+    }
+    if (kt < nk) step(kt, IntC<0>{});
+  } else {
+    lds_barrier();
+    auto step = [&](int kt, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      read_frags(smem + P * STAGE);
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_copy(min(kt + 2, nk - 1), smem + P * STAGE);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) bar();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, IntC<0>{});
+      step(kt + 1, IntC<1>{});
+    }
+    if (kt < nk) step(kt, IntC<0>{});
+  }
+  __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // no copy may land after the block ends
+
+  gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh, split);
+}
+
 // ---- fp32 FMA kernel --------------------------------------------------------
 // 64x64 tile, 256 threads; thread (tx, ty) owns rows ty*4..+4 and columns
 // {2tx, 2tx+1, 32+2tx, 33+2tx}, so the SwiGLU epilogue finds gate column c
@@ -774,6 +1169,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       }
     }
   }
+}
+
+// Byte extents the buffer-copy kernels address (their descriptors hold 32-bit
+// sizes); false when a matrix is 4 GiB or larger.
+static bool buffer_extents(GemmArgs& g, size_t w_rows) {
+  const size_t a = (static_cast<size_t>(g.M - 1) * g.lda + g.K) * 2;
+  const size_t w = w_rows * static_cast<size_t>(g.K) * 2;
+  if (a > 0xffffffffu || w > 0xffffffffu) return false;
+  g.a_bytes = static_cast<uint32_t>(a);
+  g.w_bytes = static_cast<uint32_t>(w);
+  return true;
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool SIGN1, bool OUT_F32>
@@ -874,10 +1280,20 @@ static hipError_t run_partial_narrow(GemmArgs g, int splits, hipStream_t s) {
   g.k_split = per * 64;
   g.splits = (k_tiles + per - 1) / per;
   if (g.splits_out) *g.splits_out = g.splits;
+  const int blocks = g.m_tiles * g.n_tiles * g.splits;
+  if constexpr (!SIGN1) {
+    if (buffer_extents(g, static_cast<size_t>(g.N))) {
+      if constexpr (BN == 192)
+        gemm_pp_dma_kernel<192, 4, 2, 4, OUT_F32><<<blocks, 512, 0, s>>>(g);
+      else
+        gemm_pp_dma_kernel<128, 2, 4, 4, OUT_F32><<<blocks, 512, 0, s>>>(g);
+      return hipGetLastError();
+    }
+  }
   if constexpr (BN == 192)   // 4 x 2 wavefronts of 64 x 96
-    gemm_bf16_dma_kernel<256, 192, 4, 2, 4, OUT_F32, SIGN1><<<g.m_tiles * g.n_tiles * g.splits, 512, 0, s>>>(g);
+    gemm_bf16_dma_kernel<256, 192, 4, 2, 4, OUT_F32, SIGN1><<<blocks, 512, 0, s>>>(g);
   else
-    gemm_bf16_dma_kernel<256, 128, 2, 4, 4, OUT_F32, SIGN1><<<g.m_tiles * g.n_tiles * g.splits, 512, 0, s>>>(g);
+    gemm_bf16_dma_kernel<256, 128, 2, 4, 4, OUT_F32, SIGN1><<<blocks, 512, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -907,7 +1323,10 @@ static hipError_t run_swiglu_narrow(GemmArgs g, hipStream_t s) {
   g.n_tiles = (g.N + COLS - 1) / COLS;
   g.splits = 1;
   g.k_split = g.K;
-  gemm_swiglu_kernel<COLS, SIGN1><<<g.m_tiles * g.n_tiles, 512, 0, s>>>(g);
+  if (!SIGN1 && buffer_extents(g, static_cast<size_t>(2) * g.N))
+    gemm_swiglu_pp_kernel<COLS><<<g.m_tiles * g.n_tiles, 512, 0, s>>>(g);
+  else
+    gemm_swiglu_kernel<COLS, SIGN1><<<g.m_tiles * g.n_tiles, 512, 0, s>>>(g);
   return hipGetLastError();
 }
 
