@@ -162,6 +162,31 @@ tlp_status tlp_prefill_layer(const tlp_config* cfg, const tlp_layer_weights* wei
                              const float* rope_cos, const float* rope_sin, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Bytes of the library's static scratch array (per GPU) that
+ * tlp_prefill_layer_noalloc uses as its workspace: 64 MiB. */
+#define TLP_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* tlp_prefill_layer without a workspace argument, for callers that cannot
+ * allocate device memory (work captured into HIP graphs, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, contract and result as
+ * tlp_prefill_layer, bit-identical; the workspace is a static device array of
+ * TLP_NOALLOC_SCRATCH_BYTES owned by the library (one per GPU, held until the
+ * process ends).  The call itself allocates nothing: on its first call on a
+ * GPU it looks up that array's device address (hipGetSymbolAddress, with that
+ * GPU current) and keeps it.  The GPU is the one `stream` belongs to (the
+ * current device for the null stream).
+ * A call needing more than TLP_NOALLOC_SCRATCH_BYTES
+ * (tlp_workspace_bytes(cfg, n_tokens); e.g. up to about 240 tokens of an
+ * 8B-shape layer, every decode step) returns TLP_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on one GPU uses the same array and leaves
+ * its intermediates there (layout as tlp_workspace_layout); the kernels need
+ * no part of it cleared.  Calls that overlap on one GPU (different streams,
+ * threads or processes sharing the library) race on it. */
+tlp_status tlp_prefill_layer_noalloc(const tlp_config* cfg, const tlp_layer_weights* weights,
+                                     int32_t layer, void* hidden, int32_t n_tokens,
+                                     int32_t start_position, void* k_cache, void* v_cache,
+                                     const float* rope_cos, const float* rope_sin, void* stream);
+
 /* Chunked prefill of n_tokens prompt tokens through all cfg->n_layers layers
  * (turbospark llama/prefill.rs prefill_chunk_real_llama_dense): micro-batch b
  * holds tokens [b*micro_batch, min(n_tokens, (b+1)*micro_batch)) at positions

@@ -238,3 +238,24 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    # an 8B-shape layer at 512 tokens needs ~100 MiB of workspace, above the
+    # 64 MiB static scratch: rejected before the device is touched
+    sh = synth.WORKLOADS["llama3-8b-layer"]
+    cfg = tensors.config_of(sh)
+    assert tlp.workspace_bytes(cfg, 512) > tlp.NOALLOC_SCRATCH_BYTES
+    L = tlp.lib()
+    w = _weights()
+    st = L.tlp_prefill_layer_noalloc(ctypes.byref(cfg), ctypes.byref(w), 0, FAKE, 512, 0, FAKE,
+                                     FAKE, FAKE, FAKE, None)
+    msg = L.tlp_last_error().decode()
+    assert st == tlp.TLP_ERR_WORKSPACE, msg
+    assert str(tlp.NOALLOC_SCRATCH_BYTES) in msg
+    # the usual argument checks come first
+    assert L.tlp_prefill_layer_noalloc(ctypes.byref(cfg), ctypes.byref(w), 0, FAKE, 0, 0, FAKE,
+                                       FAKE, FAKE, FAKE, None) == tlp.TLP_ERR_SHAPE
+    assert L.tlp_prefill_layer_noalloc(ctypes.byref(cfg), ctypes.byref(_weights(null="w_o")), 0,
+                                       FAKE, 4, 0, FAKE, FAKE, FAKE, FAKE,
+                                       None) == tlp.TLP_ERR_NULL

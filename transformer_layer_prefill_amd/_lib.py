@@ -19,9 +19,10 @@ TLP_F32, TLP_BF16 = 0, 1
 TLP_W_DENSE, TLP_W_SIGN1_G128 = 0, 1
 TLP_KV_ACT, TLP_KV_F16 = 0, 1
 WS_RES, WS_XN, WS_QKV, WS_ATTN, WS_ACT, WS_HEAD, WS_PART, WS_COUNT = range(8)
+NOALLOC_SCRATCH_BYTES = 64 << 20   # TLP_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("tlp_workspace_bytes", "tlp_workspace_layout", "tlp_rope_table",
-           "tlp_prefill_layer", "tlp_prefill_chunk", "tlp_argmax_rows",
+           "tlp_prefill_layer", "tlp_prefill_layer_noalloc", "tlp_prefill_chunk", "tlp_argmax_rows",
            "tlp_verify_workspace_bytes", "tlp_verify_tail", "tlp_profile_begin",
            "tlp_profile_end", "tlp_status_string", "tlp_last_error")
 KERNELS = ("attn_norm", "qkv_gemm", "qk_rope_kv", "attention", "o_gemm", "ffn_norm",
@@ -76,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.tlp_prefill_layer.argtypes = [cfgp, ctypes.POINTER(LayerWeights), i32, vp, i32, i32,
                                         vp, vp, vp, vp, vp, sz, vp]
         L.tlp_prefill_layer.restype = ctypes.c_int
+        L.tlp_prefill_layer_noalloc.argtypes = [cfgp, ctypes.POINTER(LayerWeights), i32, vp, i32,
+                                                i32, vp, vp, vp, vp, vp]
+        L.tlp_prefill_layer_noalloc.restype = ctypes.c_int
         L.tlp_prefill_chunk.argtypes = [cfgp, ctypes.POINTER(LayerWeights), vp, i32, i32, i32,
                                         vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz,
                                         vp]
@@ -156,6 +160,16 @@ def prefill_layer(cfg: Config, weights: LayerWeights, layer: int, hidden, n_toke
                                    _ptr(hidden), n_tokens, start_position, _ptr(k_cache),
                                    _ptr(v_cache), _ptr(rope_cos), _ptr(rope_sin),
                                    _ptr(workspace), wsb, _stream(stream)))
+
+
+def prefill_layer_noalloc(cfg: Config, weights: LayerWeights, layer: int, hidden, n_tokens: int,
+                          start_position: int, k_cache, v_cache, rope_cos, rope_sin,
+                          stream=None) -> None:
+    """tlp_prefill_layer with the library's static per-GPU scratch as workspace."""
+    _check(lib().tlp_prefill_layer_noalloc(ctypes.byref(cfg), ctypes.byref(weights), layer,
+                                           _ptr(hidden), n_tokens, start_position,
+                                           _ptr(k_cache), _ptr(v_cache), _ptr(rope_cos),
+                                           _ptr(rope_sin), _stream(stream)))
 
 
 def prefill_chunk(cfg: Config, layers, hidden, n_tokens: int, start_position: int,

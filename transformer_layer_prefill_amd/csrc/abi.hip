@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -447,6 +448,42 @@ struct ChunkPipe {
 
 }  // namespace
 
+// Workspace of tlp_prefill_layer_noalloc: one static array per GPU, held by
+// the loaded library until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the device
+// symbol); it looks up the array's device address once per GPU and uses that.
+static __device__ __align__(256) char scratch[TLP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+char* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
+// Device address of `scratch` on GPU `dev`, looked up with that GPU current
+// the first time (the caller's current device is restored).
+hipError_t scratch_on_device(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e == hipSuccess && prev != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (prev >= 0 && prev != dev) {
+      const hipError_t e2 = hipSetDevice(prev);
+      if (e == hipSuccess) e = e2;
+    }
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? static_cast<char*>(ptr) : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t tlp_workspace_bytes(const tlp_config* cfg, int32_t max_tokens) {
@@ -502,6 +539,39 @@ tlp_status tlp_prefill_layer(const tlp_config* cfg, const tlp_layer_weights* wei
   return run_layer(*cfg, *weights, layer, n_tokens, start_position, hidden, false, 0, hidden,
                    &parts, static_cast<char*>(k_cache), static_cast<char*>(v_cache), rope_cos,
                    rope_sin, static_cast<char*>(workspace), L, st);
+}
+
+tlp_status tlp_prefill_layer_noalloc(const tlp_config* cfg, const tlp_layer_weights* weights,
+                                     int32_t layer, void* hidden, int32_t n_tokens,
+                                     int32_t start_position, void* k_cache, void* v_cache,
+                                     const float* rope_cos, const float* rope_sin, void* stream) {
+  tlp_status s = check_config(cfg);
+  if (s != TLP_OK) return s;
+  if (layer < 0 || layer >= cfg->n_layers)
+    return fail(TLP_ERR_SHAPE, "layer %d outside [0, %d)", layer, cfg->n_layers);
+  if ((s = check_layer_weights(*cfg, weights, layer)) != TLP_OK) return s;
+  if (n_tokens <= 0) return fail(TLP_ERR_SHAPE, "n_tokens %d must be > 0", n_tokens);
+  const Layout L = layout_of(*cfg, n_tokens);
+  if (L.total > TLP_NOALLOC_SCRATCH_BYTES)
+    return fail(TLP_ERR_WORKSPACE,
+                "%d tokens need %zu bytes of workspace, above the %u-byte static scratch of "
+                "tlp_prefill_layer_noalloc (use tlp_prefill_layer with a workspace)",
+                n_tokens, L.total, TLP_NOALLOC_SCRATCH_BYTES);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  char* ws = nullptr;
+  if (e == hipSuccess) e = scratch_on_device(dev, &ws);
+  if (e != hipSuccess)
+    return fail(TLP_ERR_HIP, "scratch of device %d: %s", dev, hipGetErrorString(e));
+  if ((s = check_call(*cfg, hidden, n_tokens, start_position, k_cache, v_cache, rope_cos,
+                      rope_sin, ws, TLP_NOALLOC_SCRATCH_BYTES, n_tokens)) != TLP_OK)
+    return s;
+  g_last_error.clear();
+  int parts = 0;
+  return run_layer(*cfg, *weights, layer, n_tokens, start_position, hidden, false, 0, hidden,
+                   &parts, static_cast<char*>(k_cache), static_cast<char*>(v_cache), rope_cos,
+                   rope_sin, ws, L, st);
 }
 
 tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* layers,
