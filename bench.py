@@ -75,30 +75,53 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(sh, w, x, kc, vc, budget_s=20.0):
-    """The float64 oracle on the host cores: whole layer calls, same inputs."""
+    """The float64 oracle on the host cores: whole layer calls, same inputs,
+    with numpy's BLAS on all its threads and once more on one thread."""
     import oracle
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        cores = os.cpu_count() or 1
+        threadpool_limits = None
+        blas = os.cpu_count() or 1
     w64 = synth.widen_layer(sh, w)
     x64 = synth.widen(x, sh.dtype)
-    times = []
-    t_all = time.perf_counter()
-    while True:
-        kc64, vc64 = synth.widen(kc, sh.dtype), synth.widen(vc, sh.dtype)
-        t0 = time.perf_counter()
-        oracle.prefill_layer(sh, w64, 0, x64, sh.start, kc64, vc64)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_all > budget_s / 2 or len(times) >= 5:
-            break
-    t = float(np.mean(times))
-    return {"value": sh.n_tokens / t, "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{len(times)} full float64 oracle layer call(s) of the same workload "
-                      f"({sh.n_tokens} tokens at start {sh.start}), mean {t:.3f} s each"}
+
+    def timed_calls(max_calls, budget):
+        times = []
+        t_all = time.perf_counter()
+        while True:
+            kc64, vc64 = synth.widen(kc, sh.dtype), synth.widen(vc, sh.dtype)
+            t0 = time.perf_counter()
+            oracle.prefill_layer(sh, w64, 0, x64, sh.start, kc64, vc64)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_all > budget or len(times) >= max_calls:
+                return float(np.mean(times)), len(times)
+
+    t, n = timed_calls(5, budget_s / 2)
+    out = {"value": sh.n_tokens / t, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+           "sample": f"{n} full float64 oracle layer call(s) of the same workload "
+                     f"({sh.n_tokens} tokens at start {sh.start}), mean {t:.3f} s each",
+           "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(), "blas_threads": int(blas)}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t1, n1 = timed_calls(1, budget_s / 2)
+        out["one_thread"] = {"value": sh.n_tokens / t1, "unit": "tokens/s", "cores": 1,
+                             "sample": f"{n1} oracle layer call(s) on one BLAS thread, "
+                                       f"{t1:.3f} s each"}
+    return out
 
 
 CSRC = os.path.join(ROOT, "transformer_layer_prefill_amd", "csrc")
@@ -215,6 +238,7 @@ def bench_verify_tail(args):
     for _ in range(args.steps):
         step()
     prof = tlp.profile_end()
+    prof.pop("not_timed", None)
     kernels = {k: {"launches": n, "avg_us": round(1e3 * t / n, 3)} for k, (n, t) in prof.items() if n}
     head_us = kernels["lm_head"]["avg_us"]
     head_bytes = 2 * V * H + 2 * rows * H + 4 * rows * V
@@ -269,11 +293,12 @@ def bench_stack(args):
     ws = torch.empty(copies * tlp.workspace_bytes(cfg, min(sh.n_tokens, mb)), dtype=torch.uint8,
                      device=dev)
     logits = torch.empty(sh.vocab, dtype=torch.float32, device=dev)
+    pipeline = None if args.no_pipeline else tlp.Pipeline(sh.n_layers)
     structs = [d.struct for d in dls]
     # the profiled passes cover a few steps: one call makes ~2300 launches,
     # each bracketed by two events
     n_prof = min(args.steps, 2)
-    n_buf = args.warmup + args.steps + 2 * n_prof
+    n_buf = args.warmup + args.steps + n_prof
     hiddens = [x0.clone() for _ in range(n_buf)]
     stream = torch.cuda.current_stream(dev)
 
@@ -282,7 +307,7 @@ def bench_stack(args):
     def step(i, one_stream=False):
         tlp.prefill_chunk(cfg, structs, hiddens[i], sh.n_tokens, sh.start, mb, kcd, vcd, cosd,
                           sind, ws, final_norm=fn, lm_head=W, vocab=sh.vocab, final_eps=sh.eps,
-                          logits=logits, stream=stream,
+                          logits=logits, stream=stream, pipeline=None if one_stream else pipeline,
                           workspace_bytes=one_ws if one_stream else None)
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
@@ -299,14 +324,13 @@ def bench_stack(args):
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
     # per-kernel times from a one-stream pass (with two micro-batches in flight
-    # a kernel's events would also span the other stream's kernels).  A first
-    # pass fills the library's event pool: creating tens of thousands of events
-    # while launching starves the GPU, and the gaps land inside the brackets
-    for rep in range(2):
-        tlp.profile_begin()
-        for i in range(n_prof):
-            step(args.warmup + args.steps + rep * n_prof + i, one_stream=True)
-        prof = tlp.profile_end()
+    # a kernel's events would also span the other stream's kernels); the
+    # profiler's events are all created by profile_begin, before the pass
+    tlp.profile_begin(max_launches=4096 * n_prof)
+    for i in range(n_prof):
+        step(args.warmup + args.steps + i, one_stream=True)
+    prof = tlp.profile_end()
+    prof.pop("not_timed", None)
 
     # one chunk call captured into a HIP graph behind a copy that restores the
     # prompt rows (so every replay does the same work), replayed K times; a
@@ -459,6 +483,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     prof = tlp.profile_end()
+    prof.pop("not_timed", None)
     ms_step_prof = e0.elapsed_time(e1) / args.steps
 
     # the same K steps captured once into a HIP graph (each with its own input

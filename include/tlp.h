@@ -17,9 +17,12 @@
  *
  * Conventions for every entry point:
  *   - Every array argument is a DEVICE pointer unless marked "host".  The
- *     caller owns every buffer; the library allocates no memory and keeps no
- *     state between calls (tlp_prefill_chunk given two workspaces creates a
- *     stream and events for the call and releases them before returning).
+ *     caller owns every buffer and every stream and event the calls use (a
+ *     tlp_pipeline for two micro-batches in flight); the prefill calls
+ *     allocate nothing and keep no state between calls.  The only resources
+ *     the library creates are those of tlp_pipeline_create and
+ *     tlp_profile_begin, released by tlp_pipeline_destroy and
+ *     tlp_profile_end, and the static scratch of tlp_prefill_layer_noalloc.
  *   - Matrices are row-major.  Activations are token-major: row t of
  *     hidden [n_tokens][hidden] is token t, at absolute position
  *     start_position + t.  Projection weights are [out_features][in_features].
@@ -124,12 +127,17 @@ enum { TLP_WS_RES = 0, TLP_WS_XN = 1, TLP_WS_QKV = 2, TLP_WS_ATTN = 3, TLP_WS_AC
 
 /* Bytes of workspace a call with up to `max_tokens` tokens per micro-batch
  * needs (tlp_prefill_chunk: max_tokens = min(n_tokens, micro_batch); twice
- * that lets it run two micro-batches at once).
+ * that lets it run two micro-batches at once).  The workspace stands in for
+ * metal_prefill.rs PrefillBuffers (the lazily allocated intermediate buffers
+ * sized for the batch, reallocated when a larger batch comes): here the caller
+ * allocates it once for its largest micro-batch.
  * Returns 0 for an invalid config or max_tokens <= 0. */
 size_t tlp_workspace_bytes(const tlp_config* cfg, int32_t max_tokens);
 
 /* Byte offsets of the TLP_WS_* regions inside such a workspace (host array
- * offsets[TLP_WS_COUNT]).  Same validation as tlp_workspace_bytes. */
+ * offsets[TLP_WS_COUNT]), i.e. where the PrefillBuffers of metal_prefill.rs
+ * (normed rows, q/k/v, attention output, gate/up output, hidden) live.  Same
+ * validation as tlp_workspace_bytes. */
 tlp_status tlp_workspace_layout(const tlp_config* cfg, int32_t max_tokens, size_t* offsets);
 
 /* RoPE tables on the HOST: cos_host/sin_host [n_pos][head_dim/2] fp32 with
@@ -187,6 +195,18 @@ tlp_status tlp_prefill_layer_noalloc(const tlp_config* cfg, const tlp_layer_weig
                                      int32_t start_position, void* k_cache, void* v_cache,
                                      const float* rope_cos, const float* rope_sin, void* stream);
 
+/* Caller-owned resources for keeping two micro-batches of tlp_prefill_chunk in
+ * flight (the chunk page runs its micro-batches one after another; this
+ * library can overlap consecutive ones, which only need each other's K/V):
+ * a second stream (default priority, non-blocking) and 2*max_layers + 2
+ * events, created on the current device.  Create once, pass to any number of
+ * chunk calls with at most max_layers layers on streams of the same device,
+ * destroy when done (tlp_pipeline_destroy waits for the second stream).  Two
+ * calls in flight at once must not share a pipeline. */
+typedef struct tlp_pipeline tlp_pipeline;
+tlp_status tlp_pipeline_create(int32_t max_layers, tlp_pipeline** out);
+tlp_status tlp_pipeline_destroy(tlp_pipeline* pipeline);
+
 /* Chunked prefill of n_tokens prompt tokens through all cfg->n_layers layers
  * (turbospark llama/prefill.rs prefill_chunk_real_llama_dense): micro-batch b
  * holds tokens [b*micro_batch, min(n_tokens, (b+1)*micro_batch)) at positions
@@ -197,14 +217,16 @@ tlp_status tlp_prefill_layer_noalloc(const tlp_config* cfg, const tlp_layer_weig
  * micro-batch logits[v] = sum_k lm_head[v][k] * RMSNorm(x_last; final_norm,
  * final_eps)[k] (fp32 [vocab]); lm_head is [vocab][H] in dtype, final_norm [H]
  * in dtype.  workspace >= W = tlp_workspace_bytes(cfg, min(n_tokens, micro_batch)).
- * With workspace_bytes >= 2 W and more than one micro-batch, micro-batch b
- * uses the bytes [(b % 2) W, (b % 2 + 1) W) of the workspace and the odd ones
- * run on a second stream that the call creates (default priority,
- * non-blocking) and releases: each layer's attention of micro-batch b waits
+ * With a pipeline (tlp_pipeline_create, NULL: none), workspace_bytes >= 2 W
+ * and more than one micro-batch, micro-batch b uses the bytes
+ * [(b % 2) W, (b % 2 + 1) W) of the workspace and the odd ones run on the
+ * pipeline's second stream: each layer's attention of micro-batch b waits
  * for the K/V that micro-batch b-1 stored for that layer, so consecutive
  * micro-batches overlap one layer apart.  The second stream starts behind the
  * work already on `stream` and is joined back into it before the call
  * returns, so the call's work completes in `stream`'s order either way.
+ * A pipeline made for fewer layers is TLP_ERR_SHAPE, one made on another
+ * device than `stream`'s TLP_ERR_UNSUPPORTED.
  * While `stream` is being captured into a graph the micro-batches run one at
  * a time on it (the call then only enqueues kernels, as tlp_prefill_layer).
  * The caller tracks the cache position: a chunk must start where the previous
@@ -215,7 +237,7 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
                              const float* rope_cos, const float* rope_sin,
                              const void* final_norm, const void* lm_head, int32_t vocab,
                              float final_eps, float* logits, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             size_t workspace_bytes, tlp_pipeline* pipeline, void* stream);
 
 /* Greedy token choice (prefill page, encode_full_forward_prefill: the greedy
  * branch of the tail runs an argmax over the logits on the GPU and returns a
@@ -255,19 +277,26 @@ enum { TLP_K_ATTN_NORM = 0, TLP_K_QKV_GEMM = 1, TLP_K_QK_ROPE_KV = 2, TLP_K_ATTE
 
 /* Per-kernel GPU timing, the analog of the per-layer / per-command-buffer
  * profiling switches of metal_full_layer.rs (OXIBONSAI_PROFILE and
- * OXIBONSAI_PROFILE_GPU).  After tlp_profile_begin, every kernel launched by
- * this thread's tlp_prefill_* calls is bracketed by two HIP events recorded on
- * the call's stream.  tlp_profile_end waits for those events, writes the
- * summed elapsed milliseconds and the launch count per TLP_K_* kernel into the
- * HOST arrays total_ms[TLP_K_COUNT] and launches[TLP_K_COUNT], and stops
- * recording.  Events are created on first use and reused afterwards. */
-tlp_status tlp_profile_begin(void);
-tlp_status tlp_profile_end(double* total_ms, int32_t* launches);
+ * OXIBONSAI_PROFILE_GPU).  tlp_profile_begin creates max_launches pairs of
+ * HIP events for the calling thread; until tlp_profile_end, every kernel
+ * launched by this thread's tlp_* calls is bracketed by the next pair,
+ * recorded on the call's stream (launches past max_launches are not timed).
+ * tlp_profile_end waits for those events, writes the summed elapsed
+ * milliseconds and the launch count per TLP_K_* kernel into the HOST arrays
+ * total_ms[TLP_K_COUNT] and launches[TLP_K_COUNT] (and the number of launches
+ * not timed into *not_timed, if not NULL), and destroys the events. */
+tlp_status tlp_profile_begin(int32_t max_launches);
+tlp_status tlp_profile_end(double* total_ms, int32_t* launches, int32_t* not_timed);
 
-/* Static text of a status code. */
+/* Static text of a status code.  The codes play the part of the
+ * MetalGraphError results of the metal_prefill.rs entry points
+ * (EncodingFailed for a buffer that is too short or a dimension that does not
+ * match, ExecutionFailed for a failed command buffer). */
 const char* tlp_status_string(tlp_status status);
 
-/* Text of the calling thread's most recent error ("" if none). */
+/* Text of the calling thread's most recent error ("" if none): the message a
+ * MetalGraphError carries on the pages, kept per thread because the C ABI
+ * returns only the code. */
 const char* tlp_last_error(void);
 
 #ifdef __cplusplus

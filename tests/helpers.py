@@ -54,6 +54,12 @@ class GpuRun:
         self.sin = tensors.to_device(sin, device)
         self.ws = None
 
+    def pipeline(self):
+        """The tlp_pipeline of this run (second stream and events), made once."""
+        if getattr(self, "_pipeline", None) is None:
+            self._pipeline = self.tlp.Pipeline(self.shape.n_layers)
+        return self._pipeline
+
     def workspace(self, max_tokens, copies=1):
         nbytes = copies * self.tlp.workspace_bytes(self.cfg, max_tokens)
         if self.ws is None or self.ws.numel() < nbytes:
@@ -68,12 +74,14 @@ class GpuRun:
         self.torch.cuda.synchronize()
 
     def chunk(self, n: int, start: int, mb: int, hidden=None, head=None, pipelined=False):
-        """pipelined: pass two workspaces' worth of bytes, so consecutive
-        micro-batches alternate halves and run on two streams."""
+        """pipelined: pass two workspaces' worth of bytes and a pipeline, so
+        consecutive micro-batches alternate halves and run on two streams."""
         h = self.hidden if hidden is None else hidden
         copies = 2 if pipelined else 1
         ws = self.workspace(min(n, mb), copies)
         kw = dict(workspace_bytes=copies * self.tlp.workspace_bytes(self.cfg, min(n, mb)))
+        if pipelined:
+            kw["pipeline"] = self.pipeline()
         if head is not None:
             fn, W, vocab, logits = head
             kw.update(final_norm=fn, lm_head=W, vocab=vocab, final_eps=self.shape.eps,

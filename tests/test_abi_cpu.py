@@ -121,7 +121,7 @@ def test_chunk_argument_checks():
 
     def chunk(n=8, mb=4, head=None, norm=FAKE, logits=FAKE, vocab=10, layers=arr, wsb=wsb):
         return L.tlp_prefill_chunk(ctypes.byref(cfg), layers, FAKE, n, 0, mb, FAKE, FAKE, FAKE,
-                                   FAKE, norm, head, vocab, 1e-5, logits, FAKE, wsb, None)
+                                   FAKE, norm, head, vocab, 1e-5, logits, FAKE, wsb, None, None)
 
     assert chunk(mb=0) == tlp.TLP_ERR_SHAPE
     assert chunk(head=FAKE, norm=None) == tlp.TLP_ERR_NULL
@@ -259,3 +259,15 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
     assert L.tlp_prefill_layer_noalloc(ctypes.byref(cfg), ctypes.byref(_weights(null="w_o")), 0,
                                        FAKE, 4, 0, FAKE, FAKE, FAKE, FAKE,
                                        None) == tlp.TLP_ERR_NULL
+
+
+def test_pipeline_and_profiler_argument_checks():
+    # rejected before any HIP call: no stream or event is created
+    L = tlp.lib()
+    h = ctypes.c_void_p(123)
+    assert L.tlp_pipeline_create(0, ctypes.byref(h)) == tlp.TLP_ERR_SHAPE
+    assert h.value is None                      # *out is cleared on failure
+    assert L.tlp_pipeline_create(4, None) == tlp.TLP_ERR_NULL
+    assert L.tlp_pipeline_destroy(None) == tlp.TLP_OK
+    assert L.tlp_profile_begin(0) == tlp.TLP_ERR_SHAPE
+    assert L.tlp_profile_end(None, None, None) == tlp.TLP_ERR_NULL

@@ -23,7 +23,8 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # TLP_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("tlp_workspace_bytes", "tlp_workspace_layout", "tlp_rope_table",
            "tlp_prefill_layer", "tlp_prefill_layer_noalloc", "tlp_prefill_chunk", "tlp_argmax_rows",
-           "tlp_verify_workspace_bytes", "tlp_verify_tail", "tlp_profile_begin",
+           "tlp_verify_workspace_bytes", "tlp_verify_tail", "tlp_pipeline_create",
+           "tlp_pipeline_destroy", "tlp_profile_begin",
            "tlp_profile_end", "tlp_status_string", "tlp_last_error")
 KERNELS = ("attn_norm", "qkv_gemm", "qk_rope_kv", "attention", "o_gemm", "ffn_norm",
            "gate_up_gemm", "down_gemm", "final_norm", "lm_head", "out_rows", "swiglu",
@@ -82,7 +83,11 @@ def lib() -> ctypes.CDLL:
         L.tlp_prefill_layer_noalloc.restype = ctypes.c_int
         L.tlp_prefill_chunk.argtypes = [cfgp, ctypes.POINTER(LayerWeights), vp, i32, i32, i32,
                                         vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz,
-                                        vp]
+                                        vp, vp]
+        L.tlp_pipeline_create.argtypes = [i32, ctypes.POINTER(vp)]
+        L.tlp_pipeline_create.restype = ctypes.c_int
+        L.tlp_pipeline_destroy.argtypes = [vp]
+        L.tlp_pipeline_destroy.restype = ctypes.c_int
         L.tlp_prefill_chunk.restype = ctypes.c_int
         L.tlp_argmax_rows.argtypes = [vp, i32, i32, ctypes.c_int64, vp, vp]
         L.tlp_argmax_rows.restype = ctypes.c_int
@@ -91,9 +96,9 @@ def lib() -> ctypes.CDLL:
         L.tlp_verify_tail.argtypes = [cfgp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp,
                                       sz, vp]
         L.tlp_verify_tail.restype = ctypes.c_int
-        L.tlp_profile_begin.argtypes = []
+        L.tlp_profile_begin.argtypes = [i32]
         L.tlp_profile_begin.restype = ctypes.c_int
-        L.tlp_profile_end.argtypes = [vp, vp]
+        L.tlp_profile_end.argtypes = [vp, vp, vp]
         L.tlp_profile_end.restype = ctypes.c_int
         L.tlp_status_string.argtypes = [ctypes.c_int]
         L.tlp_status_string.restype = ctypes.c_char_p
@@ -172,18 +177,43 @@ def prefill_layer_noalloc(cfg: Config, weights: LayerWeights, layer: int, hidden
                                            _ptr(rope_sin), _stream(stream)))
 
 
+class Pipeline:
+    """A tlp_pipeline: the second stream and events that let prefill_chunk keep
+    two micro-batches in flight.  Made on the current device; released by
+    close() or when garbage-collected."""
+
+    def __init__(self, max_layers: int):
+        h = ctypes.c_void_p()
+        _check(lib().tlp_pipeline_create(max_layers, ctypes.byref(h)))
+        self.handle = h.value
+        self.max_layers = max_layers
+
+    def close(self) -> None:
+        if self.handle:
+            h, self.handle = self.handle, None
+            _check(lib().tlp_pipeline_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def prefill_chunk(cfg: Config, layers, hidden, n_tokens: int, start_position: int,
                   micro_batch: int, k_cache, v_cache, rope_cos, rope_sin, workspace,
                   final_norm=None, lm_head=None, vocab: int = 0, final_eps: float = 0.0,
-                  logits=None, workspace_bytes: int | None = None, stream=None) -> None:
+                  logits=None, workspace_bytes: int | None = None, pipeline=None,
+                  stream=None) -> None:
     arr = (LayerWeights * len(layers))(*layers)
     wsb = workspace_bytes if workspace_bytes is not None else \
         workspace.numel() * workspace.element_size()
+    pipe = pipeline.handle if isinstance(pipeline, Pipeline) else pipeline
     _check(lib().tlp_prefill_chunk(ctypes.byref(cfg), arr, _ptr(hidden), n_tokens,
                                    start_position, micro_batch, _ptr(k_cache), _ptr(v_cache),
                                    _ptr(rope_cos), _ptr(rope_sin), _ptr(final_norm),
                                    _ptr(lm_head), vocab, final_eps, _ptr(logits),
-                                   _ptr(workspace), wsb, _stream(stream)))
+                                   _ptr(workspace), wsb, pipe, _stream(stream)))
 
 
 def argmax_rows(logits, rows: int, vocab: int, ld: int, token_ids, stream=None) -> None:
@@ -205,13 +235,17 @@ def verify_tail(cfg: Config, hidden, n_rows: int, final_norm, lm_head, vocab: in
                                  _ptr(token_ids), _ptr(workspace), wsb, _stream(stream)))
 
 
-def profile_begin() -> None:
-    _check(lib().tlp_profile_begin())
+def profile_begin(max_launches: int = 8192) -> None:
+    _check(lib().tlp_profile_begin(max_launches))
 
 
 def profile_end() -> dict:
-    """{kernel name: (launches, total milliseconds)} since profile_begin()."""
+    """{kernel name: (launches, total milliseconds)} since profile_begin();
+    launches past its capacity are not timed (key "not_timed")."""
     ms = np.zeros(len(KERNELS), dtype=np.float64)
     n = np.zeros(len(KERNELS), dtype=np.int32)
-    _check(lib().tlp_profile_end(ms.ctypes.data, n.ctypes.data))
-    return {k: (int(n[i]), float(ms[i])) for i, k in enumerate(KERNELS)}
+    dropped = ctypes.c_int32(0)
+    _check(lib().tlp_profile_end(ms.ctypes.data, n.ctypes.data, ctypes.byref(dropped)))
+    out = {k: (int(n[i]), float(ms[i])) for i, k in enumerate(KERNELS)}
+    out["not_timed"] = (int(dropped.value), 0.0)
+    return out

@@ -14,11 +14,21 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <new>
 #include <string>
 #include <vector>
 
 #include "../../include/tlp.h"
 #include "launch.h"
+
+// A caller-owned pipeline handle (tlp_pipeline_create): the second stream and
+// the events that let tlp_prefill_chunk keep two micro-batches in flight.
+struct tlp_pipeline {
+  int device = -1;
+  int max_layers = 0;
+  hipStream_t second = nullptr;
+  std::vector<hipEvent_t> ev;   // [2][max_layers] K/V-stored events, then start, end
+};
 
 namespace {
 
@@ -188,44 +198,49 @@ tlp_status check_call(const tlp_config& c, void* hidden, int n, int start, void*
 }
 
 // ---- per-kernel timing with HIP events (tlp_profile_begin / tlp_profile_end) --
-// While a thread has profiling on, every launch it makes is bracketed by two
-// events recorded on the launch's own stream; tlp_profile_end waits for them
-// and sums the elapsed times per kernel.
+// tlp_profile_begin creates a fixed number of event pairs for the calling
+// thread; while profiling is on, every launch the thread makes is bracketed by
+// the next pair, recorded on the launch's own stream (launches beyond the
+// capacity are counted as not timed).  tlp_profile_end waits for the events,
+// sums the elapsed times per kernel and destroys them.
 struct ProfRecord {
   int kernel;
   hipEvent_t start, stop;
 };
 thread_local bool g_prof_on = false;
-thread_local std::vector<ProfRecord> g_prof;
-thread_local std::vector<hipEvent_t> g_event_pool;
-
-hipError_t take_event(hipEvent_t* e) {
-  if (!g_event_pool.empty()) {
-    *e = g_event_pool.back();
-    g_event_pool.pop_back();
-    return hipSuccess;
-  }
-  return hipEventCreate(e);
-}
+thread_local std::vector<ProfRecord> g_prof;   // created pairs; kernel < 0: not used yet
+thread_local size_t g_prof_used = 0;
+thread_local int32_t g_prof_dropped = 0;
 
 struct ProfScope {
   int kernel;
   hipStream_t s;
-  hipEvent_t start = nullptr;
+  ProfRecord* rec = nullptr;
   hipError_t err = hipSuccess;
   ProfScope(int k, hipStream_t st) : kernel(k), s(st) {
     if (!g_prof_on) return;
-    if ((err = take_event(&start)) == hipSuccess) err = hipEventRecord(start, s);
+    if (g_prof_used == g_prof.size()) {
+      ++g_prof_dropped;
+      return;
+    }
+    rec = &g_prof[g_prof_used++];
+    rec->kernel = kernel;
+    err = hipEventRecord(rec->start, s);
   }
   hipError_t finish() {
-    if (!g_prof_on || err != hipSuccess) return err;
-    hipEvent_t stop;
-    if ((err = take_event(&stop)) != hipSuccess) return err;
-    if ((err = hipEventRecord(stop, s)) != hipSuccess) return err;
-    g_prof.push_back({kernel, start, stop});
-    return hipSuccess;
+    if (!rec || err != hipSuccess) return err;
+    return err = hipEventRecord(rec->stop, s);
   }
 };
+
+void prof_release() {
+  for (ProfRecord& r : g_prof) {
+    if (r.start) (void)hipEventDestroy(r.start);
+    if (r.stop) (void)hipEventDestroy(r.stop);
+  }
+  g_prof.clear();
+  g_prof_used = 0;
+}
 
 #define TLP_LAUNCH(kid, expr)                                                     \
   do {                                                                            \
@@ -408,41 +423,29 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   return TLP_OK;
 }
 
-// Two micro-batches of a chunk in flight: a second stream for the odd
-// micro-batches, started behind the work already on the caller's stream, and
-// per (stream parity, layer) an event recorded once that micro-batch's K/V of
-// the layer are in the cache.  The destructor joins the second stream into
-// the caller's (all of the call's work then completes in the caller's stream
-// order, also after an error) and releases the stream and the events; HIP
-// frees them once their pending work has completed.
+// Two micro-batches of a chunk in flight: the caller's pipeline handle holds a
+// second stream for the odd micro-batches and, per (stream parity, layer), an
+// event recorded once that micro-batch's K/V of the layer are in the cache,
+// plus a start and an end event.  ChunkPipe starts the second stream behind
+// the work already on the caller's stream and, when it goes out of scope,
+// joins it back (all of the call's work then completes in the caller's stream
+// order, also after an error).
 struct ChunkPipe {
-  hipStream_t main = nullptr, second = nullptr;
-  std::vector<hipEvent_t> ev;   // [2][n_layers], then start and end
-  int n_layers = 0;
+  hipStream_t main = nullptr;
+  tlp_pipeline* p = nullptr;
 
-  hipError_t init(hipStream_t s, int layers) {
+  hipError_t init(hipStream_t s, tlp_pipeline* pipe) {
     main = s;
-    n_layers = layers;
-    hipError_t e = hipStreamCreateWithFlags(&second, hipStreamNonBlocking);
-    if (e != hipSuccess) {
-      second = nullptr;
-      return e;
-    }
-    ev.assign(2 * layers + 2, nullptr);
-    for (hipEvent_t& x : ev)
-      if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventRecord(ev[2 * layers], main)) != hipSuccess) return e;
-    return hipStreamWaitEvent(second, ev[2 * layers], 0);
+    p = pipe;
+    hipError_t e = hipEventRecord(p->ev[2 * p->max_layers], main);
+    if (e != hipSuccess) return e;
+    return hipStreamWaitEvent(p->second, p->ev[2 * p->max_layers], 0);
   }
-  hipEvent_t kv_event(int parity, int layer) const { return ev[parity * n_layers + layer]; }
+  hipEvent_t kv_event(int parity, int layer) const { return p->ev[parity * p->max_layers + layer]; }
   ~ChunkPipe() {
-    if (second) {
-      hipEvent_t end = ev.empty() ? nullptr : ev.back();
-      if (end && hipEventRecord(end, second) == hipSuccess) (void)hipStreamWaitEvent(main, end, 0);
-      (void)hipStreamDestroy(second);
-    }
-    for (hipEvent_t x : ev)
-      if (x) (void)hipEventDestroy(x);
+    if (!p) return;
+    hipEvent_t end = p->ev[2 * p->max_layers + 1];
+    if (hipEventRecord(end, p->second) == hipSuccess) (void)hipStreamWaitEvent(main, end, 0);
   }
 };
 
@@ -580,7 +583,7 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
                              const float* rope_cos, const float* rope_sin,
                              const void* final_norm, const void* lm_head, int32_t vocab,
                              float final_eps, float* logits, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             size_t workspace_bytes, tlp_pipeline* pipeline, void* stream) {
   tlp_status s = check_config(cfg);
   if (s != TLP_OK) return s;
   if (!layers) return fail(TLP_ERR_NULL, "layers is NULL");
@@ -611,8 +614,17 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
   // the previous micro-batch's K/V of that layer: consecutive micro-batches
   // overlap, one layer apart.
   const int n_mb = (n_tokens + mb - 1) / mb;
-  bool pipelined = n_mb > 1 && workspace_bytes / 2 >= L.total;
+  bool pipelined = pipeline && n_mb > 1 && workspace_bytes / 2 >= L.total;
   if (pipelined) {
+    if (pipeline->max_layers < cfg->n_layers)
+      return fail(TLP_ERR_SHAPE, "pipeline made for %d layers, the config has %d",
+                  pipeline->max_layers, cfg->n_layers);
+    int dev = -1;
+    const hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TLP_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+    if (dev != pipeline->device)
+      return fail(TLP_ERR_UNSUPPORTED, "pipeline made on device %d, the stream is on device %d",
+                  pipeline->device, dev);
     // a stream being captured into a graph gets the one-stream order: the
     // call then enqueues kernels on it only
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -622,15 +634,15 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
   {
     ChunkPipe pipe;
     if (pipelined) {
-      const hipError_t e = pipe.init(st, cfg->n_layers);
+      const hipError_t e = pipe.init(st, pipeline);
       if (e != hipSuccess)
-        return fail(TLP_ERR_HIP, "second stream for the chunk: %s", hipGetErrorString(e));
+        return fail(TLP_ERR_HIP, "starting the second stream: %s", hipGetErrorString(e));
     }
     for (int b = 0; b < n_mb; ++b) {
       const int off = b * mb;
       const int m = n_tokens - off < mb ? n_tokens - off : mb;
       const int half = pipelined ? (b & 1) : 0;
-      hipStream_t sb = half ? pipe.second : st;
+      hipStream_t sb = half ? pipeline->second : st;
       char* wsb = ws + half * L.total;
       char* rows = static_cast<char*>(hidden) + static_cast<size_t>(off) * row_bytes;
       int parts = 0;
@@ -657,6 +669,46 @@ tlp_status tlp_prefill_chunk(const tlp_config* cfg, const tlp_layer_weights* lay
     TLP_LAUNCH(TLP_K_FINAL_NORM, launch_rownorm(act, r, s));
     TLP_LAUNCH(TLP_K_LM_HEAD, launch_lm_head(act, xh, lm_head, logits, vocab, cfg->hidden, s));
   }
+  return TLP_OK;
+}
+
+tlp_status tlp_pipeline_create(int32_t max_layers, tlp_pipeline** out) {
+  if (!out) return fail(TLP_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  if (max_layers <= 0) return fail(TLP_ERR_SHAPE, "max_layers %d must be > 0", max_layers);
+  tlp_pipeline* p = new (std::nothrow) tlp_pipeline();
+  if (!p) return fail(TLP_ERR_HIP, "out of host memory");
+  p->max_layers = max_layers;
+  hipError_t e = hipGetDevice(&p->device);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->second, hipStreamNonBlocking);
+  if (e == hipSuccess) {
+    p->ev.assign(2 * static_cast<size_t>(max_layers) + 2, nullptr);
+    for (hipEvent_t& x : p->ev)
+      if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) break;
+  }
+  if (e != hipSuccess) {
+    tlp_pipeline_destroy(p);
+    return fail(TLP_ERR_HIP, "pipeline resources: %s", hipGetErrorString(e));
+  }
+  *out = p;
+  return TLP_OK;
+}
+
+tlp_status tlp_pipeline_destroy(tlp_pipeline* p) {
+  if (!p) return TLP_OK;
+  hipError_t first = hipSuccess;
+  if (p->second) first = hipStreamSynchronize(p->second);
+  for (hipEvent_t x : p->ev)
+    if (x) {
+      const hipError_t e = hipEventDestroy(x);
+      if (first == hipSuccess) first = e;
+    }
+  if (p->second) {
+    const hipError_t e = hipStreamDestroy(p->second);
+    if (first == hipSuccess) first = e;
+  }
+  delete p;
+  if (first != hipSuccess) return fail(TLP_ERR_HIP, "pipeline release: %s", hipGetErrorString(first));
   return TLP_OK;
 }
 
@@ -727,17 +779,24 @@ tlp_status tlp_verify_tail(const tlp_config* cfg, const void* hidden, int32_t n_
   return TLP_OK;
 }
 
-tlp_status tlp_profile_begin(void) {
-  for (auto& r : g_prof) {
-    g_event_pool.push_back(r.start);
-    g_event_pool.push_back(r.stop);
+tlp_status tlp_profile_begin(int32_t max_launches) {
+  if (max_launches <= 0) return fail(TLP_ERR_SHAPE, "max_launches %d must be > 0", max_launches);
+  prof_release();
+  g_prof_dropped = 0;
+  g_prof.assign(static_cast<size_t>(max_launches), ProfRecord{-1, nullptr, nullptr});
+  for (ProfRecord& r : g_prof) {
+    hipError_t e = hipEventCreate(&r.start);
+    if (e == hipSuccess) e = hipEventCreate(&r.stop);
+    if (e != hipSuccess) {
+      prof_release();
+      return fail(TLP_ERR_HIP, "profile events: %s", hipGetErrorString(e));
+    }
   }
-  g_prof.clear();
   g_prof_on = true;
   return TLP_OK;
 }
 
-tlp_status tlp_profile_end(double* total_ms, int32_t* launches) {
+tlp_status tlp_profile_end(double* total_ms, int32_t* launches, int32_t* not_timed) {
   if (!total_ms || !launches) return fail(TLP_ERR_NULL, "output arrays are NULL");
   g_prof_on = false;
   for (int k = 0; k < TLP_K_COUNT; ++k) {
@@ -745,7 +804,8 @@ tlp_status tlp_profile_end(double* total_ms, int32_t* launches) {
     launches[k] = 0;
   }
   tlp_status st = TLP_OK;
-  for (auto& r : g_prof) {
+  for (size_t i = 0; i < g_prof_used; ++i) {
+    const ProfRecord& r = g_prof[i];
     float ms = 0.f;
     hipError_t e = hipEventSynchronize(r.stop);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
@@ -753,10 +813,9 @@ tlp_status tlp_profile_end(double* total_ms, int32_t* launches) {
       st = fail(TLP_ERR_HIP, "profile events: %s", hipGetErrorString(e));
     total_ms[r.kernel] += ms;
     launches[r.kernel] += 1;
-    g_event_pool.push_back(r.start);
-    g_event_pool.push_back(r.stop);
   }
-  g_prof.clear();
+  if (not_timed) *not_timed = g_prof_dropped;
+  prof_release();
   return st;
 }
 
