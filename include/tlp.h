@@ -118,8 +118,11 @@ typedef struct {
 /* Workspace regions (for tlp_workspace_layout).  After tlp_prefill_layer they
  * hold that call's intermediates: RES fp32 [n][H] the residual stream, i.e.
  * the layer's output before it is rounded to dtype; XN the FFN-normed rows
- * [n][H] (dtype); QKV [n][(nq+2nkv)hd] (dtype) with Q normed and roped in place
- * and K, V as projected; ATTN [n][nq*hd] attention output (dtype); ACT [n][I]
+ * [n][H] (dtype); QKV [n][(nq+2nkv)hd] (dtype) whose Q columns hold the normed,
+ * roped queries (its K and V columns hold the projected K and V only with fp32
+ * activations; with bf16 ones K and V go from the projection's split-K sums
+ * straight to the cache and those columns are not written); ATTN [n][nq*hd]
+ * attention output (dtype); ACT [n][I]
  * SwiGLU output (dtype); HEAD fp32 [H] normed last row (chunk with a head);
  * PART fp32 split-K slices of the output and down projections (bf16 only). */
 enum { TLP_WS_RES = 0, TLP_WS_XN = 1, TLP_WS_QKV = 2, TLP_WS_ATTN = 3, TLP_WS_ACT = 4,
