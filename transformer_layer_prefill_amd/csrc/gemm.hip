@@ -1094,6 +1094,170 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_pp_dma_kernel(GemmArgs g) {
   gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh, split);
 }
 
+// ---- dense 256x256 projections: each wavefront's copies spread over its MFMAs --
+// The tiles, swizzle, K slices, fragment double-buffering and epilogues of
+// gemm_bf16_dma_kernel at BM = BN = 256, where a whole K tile of fragments does
+// not fit beside the accumulators and the two-group schedule of
+// gemm_pp_dma_kernel is not possible.  Instead of issuing its share of the
+// next-but-one tile's copies in one burst after the barrier (a copy
+// instruction holds its wavefront until the load path accepts it, so a burst
+// stalls the MFMAs behind it), every wavefront issues them one at a time
+// between the MFMAs of the k-step that follows the barrier.  Copies use
+// buffer-resource loads: wavefront w copies activation blocks A_PW*w .. and
+// weight blocks B_PW*w .. (1 KB = 8 rows of 128 bytes; lane l fetches chunk
+// (l & 7) ^ swz8(row) of row l >> 3).  Past the last tile the copies repeat
+// the last tile into the stage nobody reads any more (a branch around them
+// would split the scheduled MFMA group); all copies are waited for before the
+// epilogue.
+template <int BN, int WM, int WN, int EPI, bool OUT_F32>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_dma_spread_kernel(GemmArgs g) {
+  constexpr int BM = 256, BK = 64, ROWB = 128, NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;   // copies per wavefront
+  constexpr int CPW = A_PW + B_PW;
+  static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "copy split");
+  static_assert((FM * FN) % CPW == 0, "copies spread evenly over a k-step's MFMAs");
+  static_assert(EPI != 2 || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int wi = xcd_tile(blockIdx.x, gridDim.x);
+  const int split = wi % g.splits, t = wi / g.splits;
+  const int mt = t % g.m_tiles, nt = t / g.m_tiles;
+  const int m0 = mt * BM;
+  const int k_begin = split * g.k_split;
+  const int k_end = min(g.K, k_begin + g.k_split);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 31, lh = lane >> 5;
+  // weight row of B-tile row r (SwiGLU: each wavefront column holds TN/2 gate
+  // rows then the TN/2 up rows of the same output columns); rows past N are
+  // clamped, their products land in discarded outputs
+  auto b_row = [&](int r) -> int {
+    if constexpr (EPI == 2) {
+      const int w = r / TN, rr = r % TN;
+      const int jj = min(nt * (BN / 2) + w * (TN / 2) + rr % (TN / 2), g.N - 1);
+      return rr >= TN / 2 ? g.up_row + jj : jj;
+    } else {
+      return min(nt * BN + r, g.N - 1);
+    }
+  };
+  const int drow = lane >> 3, dslot = lane & 7;
+  uint32_t c_src[CPW];   // copy j < A_PW is an activation copy
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    if (j < A_PW) {
+      const int row = (A_PW * wave + j) * 8 + drow;
+      c_src[j] = (static_cast<uint32_t>(min(m0 + row, g.M - 1)) * g.lda + (dslot ^ swz8(row)) * 8) * 2;
+    } else {
+      const int row = (B_PW * wave + j - A_PW) * 8 + drow;
+      c_src[j] = (static_cast<uint32_t>(b_row(row)) * g.K + (dslot ^ swz8(row)) * 8) * 2;
+    }
+  }
+  const i32x4_t a_rsrc = buffer_rsrc(g.A, g.a_bytes);
+  const i32x4_t b_rsrc = buffer_rsrc(g.W, g.w_bytes);
+  auto kbyte = [&](int kt) { return __builtin_amdgcn_readfirstlane((k_begin + kt * BK) * 2); };
+  auto copy = [&](int kt, int j) __attribute__((always_inline)) {
+    char* st = smem + (kt & 1) * STAGE;
+    if (j < A_PW) dma16_buf(a_rsrc, c_src[j], kbyte(kt), st + (A_PW * wave + j) * 1024);
+    else dma16_buf(b_rsrc, c_src[j], kbyte(kt), st + A_BYTES + (B_PW * wave + j - A_PW) * 1024);
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // fragment rows are 32-aligned, so swz8(row) = swz8(lr)
+  const int sw = swz8(lr);
+  const int a_off = (wm * TM + lr) * ROWB, b_off = A_BYTES + (wn * TN + lr) * ROWB;
+  int ch[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) ch[kk] = ((kk * 2 + lh) ^ sw) << 4;
+  bf16x8_t af0[FM], bf0[FN], af1[FM], bf1[FN];
+#define TLP_FRAGS(AF, BF, ST, C)                                                             \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i) AF[i] =                                     \
+      *reinterpret_cast<const bf16x8_t*>((ST) + a_off + i * 32 * ROWB + (C));                \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) BF[j] =                                     \
+      *reinterpret_cast<const bf16x8_t*>((ST) + b_off + j * 32 * ROWB + (C));
+#define TLP_MMA(AF, BF)                                                                      \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i)                                             \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AF[i], BF[j], acc[i][j], 0, 0, 0);
+
+  const int nk = (k_end - k_begin) / BK;
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) copy(0, j);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) copy(1, j);
+    __builtin_amdgcn_s_waitcnt(VmWait<CPW>::imm);
+  } else {
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+  }
+  lds_barrier();
+  TLP_FRAGS(af0, bf0, smem, ch[0])
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+
+  // per 64-wide tile kt: four 16-wide k-steps, fragments of step s+1 read
+  // during the MFMAs of step s; after step 2's MFMAs wait for tile kt+1,
+  // barrier (every wavefront has read all of tile kt), then step 3's MFMAs
+  // with the copies of tile kt+2 into tile kt's stage between them
+  int kt = 0;
+  for (; kt + 1 < nk; ++kt) {
+    const char* st = smem + (kt & 1) * STAGE;
+    TLP_FRAGS(af1, bf1, st, ch[1])
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af0, bf0)
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_FRAGS(af0, bf0, st, ch[2])
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af1, bf1)
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_FRAGS(af1, bf1, st, ch[3])
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af0, bf0)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wavefront's copies of tile kt+1
+    lds_barrier();
+    const char* st1 = smem + ((kt + 1) & 1) * STAGE;
+    TLP_FRAGS(af0, bf0, st1, ch[0])
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) copy(min(kt + 2, nk - 1), j);
+    TLP_MMA(af1, bf1)
+    // masks: 0x100 LDS read, 0x8 MFMA, 0x20 vector memory read
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, (FM * FN) / CPW, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    const char* st = smem + (kt & 1) * STAGE;
+    TLP_FRAGS(af1, bf1, st, ch[1])
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af0, bf0)
+    TLP_FRAGS(af0, bf0, st, ch[2])
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af1, bf1)
+    TLP_FRAGS(af1, bf1, st, ch[3])
+    __builtin_amdgcn_sched_barrier(0);
+    TLP_MMA(af0, bf0)
+    TLP_MMA(af1, bf1)
+  }
+#undef TLP_FRAGS
+#undef TLP_MMA
+  __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // no copy may land after the block ends
+  gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh, split);
+}
+
 // ---- fp32 FMA kernel --------------------------------------------------------
 // 64x64 tile, 256 threads; thread (tx, ty) owns rows ty*4..+4 and columns
 // {2tx, 2tx+1, 32+2tx, 33+2tx}, so the SwiGLU epilogue finds gate column c
@@ -1200,6 +1364,12 @@ static hipError_t run_bf16(GemmArgs g, int splits, hipStream_t s) {
   const int blocks = g.m_tiles * g.n_tiles * g.splits;
   if (g.splits_out) *g.splits_out = g.splits;
   if (dma) {
+    if constexpr (!SIGN1 && BM == 256 && BN == 256) {
+      if (buffer_extents(g, EPI == 2 ? static_cast<size_t>(2) * g.N : static_cast<size_t>(g.N))) {
+        gemm_dma_spread_kernel<BN, WM, WN, EPI, OUT_F32><<<blocks, WM * WN * 64, 0, s>>>(g);
+        return hipGetLastError();
+      }
+    }
     gemm_bf16_dma_kernel<BM, BN, WM, WN, EPI, OUT_F32, SIGN1><<<blocks, WM * WN * 64, 0, s>>>(g);
     return hipGetLastError();
   }
