@@ -703,37 +703,40 @@ __global__ __launch_bounds__(512) void gemm_swiglu_kernel(GemmArgs g) {
 // ---- gate/up + SwiGLU, two wavefront groups half a tile apart (dense) --------
 // The block, wavefront tiles, LDS swizzle and SwiGLU epilogue are those of
 // gemm_swiglu_kernel (COLS output columns: 112 or 96).  What differs is
-// when the copies are issued.  A copy instruction holds up the wavefront that
-// issues it until the CU's load path accepts it (about 16 cycles per KB), so
-// copies issued in a burst before a run of MFMAs stall those MFMAs.  Here the
-// eight wavefronts form two groups, waves 0-3 (token rows 0-127) and 4-7
-// (rows 128-255), one wavefront of each per SIMD, that run half a K tile
-// apart; each phase ends in a workgroup barrier:
+// when the copies are issued and how far ahead.  A copy instruction holds up
+// the wavefront that issues it until the CU's load path accepts it (about 16
+// cycles per KB), so copies issued in a burst before a run of MFMAs stall
+// those MFMAs.  Here the eight wavefronts form two groups, waves 0-3 (token
+// rows 0-127) and 4-7 (rows 128-255), one wavefront of each per SIMD, that run
+// half a K tile apart; each phase ends in a workgroup barrier:
 //   phase 2kt    group 0 copies the activation tile of tile kt+1 into the
 //                stage freed by phase 2kt-1, then reads its fragments of tile
 //                kt from LDS; group 1 runs the MFMAs of tile kt-1 with the
-//                weight tile of tile kt+1 copied between them (one copy
-//                instruction every four MFMAs of the second k-step);
+//                weight tile of tile kt+2 copied between them (one copy
+//                instruction every four MFMAs of the second k-step) into the
+//                ring stage of tile kt-1;
 //   phase 2kt+1  group 0 runs the MFMAs of tile kt; group 1 reads tile kt.
 // So the MFMA pipe of each SIMD is fed by one group while the other reads.
-// Every wavefront waits for its copies of tile kt+1 before the barrier that
-// ends phase 2kt+1.  Group 1's copies past the last tile re-copy the last
-// tile's weights into a stage nobody reads any more (a branch around them
-// would split the scheduled MFMA block); all copies are waited for before the
+// The activation tiles (read from L2) sit in two stages; the weight tiles,
+// streamed from HBM, in a ring of three, so each weight copy has two tiles
+// of time to land.  Every wavefront waits for its copies of tile kt+1 before
+// the barrier that ends phase 2kt+1.  Copies past the last tile re-copy the
+// last tile into a stage nobody reads any more (a branch around them would
+// split the scheduled MFMA block); all copies are waited for before the
 // epilogue.
 template <int N> struct IntC { static constexpr int value = N; };
 
 template <int COLS>
 __global__ __launch_bounds__(512) void gemm_swiglu_pp_kernel(GemmArgs g) {
   constexpr int BM = 256, BR = 2 * COLS, BK = 64, ROWB = 128;
-  constexpr int FM = 4, FN = COLS / 16;                     // 16x16 fragments per wavefront
+  constexpr int FM = 4, FN = COLS / 16;
   constexpr int A_BYTES = BM * ROWB, B_BYTES = BR * ROWB;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_PW = A_BYTES / 1024 / 4;                  // 8 activation blocks per group-0 wavefront
-  constexpr int B_PW = B_BYTES / 1024 / 4;                  // 8, 7 or 6 weight blocks per group-1 wavefront
+  constexpr int A_PW = A_BYTES / 1024 / 4;
+  constexpr int B_PW = B_BYTES / 1024 / 4;
+  constexpr int B_BASE = 2 * A_BYTES;   // weight ring of three stages after the two activation stages
   static_assert(COLS % 16 == 0 && B_BYTES % 4096 == 0 && 4 * B_PW <= FM * FN, "tile shape");
   typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * A_BYTES + 3 * B_BYTES];
 
   const int wi = xcd_tile(blockIdx.x, gridDim.x);
   const int mt = wi % g.m_tiles, nt = wi / g.m_tiles;
@@ -745,10 +748,6 @@ __global__ __launch_bounds__(512) void gemm_swiglu_pp_kernel(GemmArgs g) {
   const int l16 = lane & 15, lq = lane >> 4;
   const int nk = g.K / BK;
 
-  // Copy streams: a 1 KB block is 8 rows of 128 bytes; lane l fetches chunk
-  // (l & 7) ^ swz16(row) of row l >> 3.  Group-0 wavefront cw copies
-  // activation blocks 8cw .. 8cw+7, group-1 wavefront cw weight blocks
-  // B_PW*cw .. (32-bit byte offsets from the matrix bases).
   const int drow = lane >> 3, dslot = lane & 7;
   constexpr int C_PW = A_PW > B_PW ? A_PW : B_PW;
   uint32_t c_src[C_PW];
@@ -763,19 +762,13 @@ __global__ __launch_bounds__(512) void gemm_swiglu_pp_kernel(GemmArgs g) {
     }
   }
   const i32x4_t c_rsrc = grp == 0 ? buffer_rsrc(g.A, g.a_bytes) : buffer_rsrc(g.W, g.w_bytes);
-  const int c_lds = grp == 0 ? cw * A_PW * 1024 : A_BYTES + cw * B_PW * 1024;
   auto kbyte = [&](int kt) { return __builtin_amdgcn_readfirstlane(kt * BK * 2); };
-  auto copy = [&](int kt, char* st, int j) __attribute__((always_inline)) {
-    dma16_buf(c_rsrc, c_src[j], kbyte(kt), st + c_lds + j * 1024);
+  // group 0: activation tile kt into stage kt & 1; group 1: weight tile kt into ring slot kt % 3
+  auto a_copy = [&](int kt, int j) __attribute__((always_inline)) {
+    dma16_buf(c_rsrc, c_src[j], kbyte(kt), smem + (kt & 1) * A_BYTES + (cw * A_PW + j) * 1024);
   };
-  auto copy_tile = [&](int kt, char* st) __attribute__((always_inline)) {
-    if (grp == 0) {
-#pragma unroll
-      for (int j = 0; j < A_PW; ++j) copy(kt, st, j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < B_PW; ++j) copy(kt, st, j);
-    }
+  auto b_copy = [&](int kt, int slot, int j) __attribute__((always_inline)) {
+    dma16_buf(c_rsrc, c_src[j], kbyte(kt), smem + B_BASE + slot * B_BYTES + (cw * B_PW + j) * 1024);
   };
 
   f32x4 acc[FM][FN];
@@ -784,21 +777,20 @@ __global__ __launch_bounds__(512) void gemm_swiglu_pp_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment rows are 16-aligned, so every row this lane reads has swz16(l16)
   const int sw = swz16(l16);
-  const int a_off = (wm * 64 + l16) * ROWB, b_off = A_BYTES + (wn * COLS + l16) * ROWB;
+  const int a_off = (wm * 64 + l16) * ROWB, b_off = (wn * COLS + l16) * ROWB;
   const int ch0 = ((0 * 4 + lq) ^ sw) << 4, ch1 = ((1 * 4 + lq) ^ sw) << 4;
   bf16x8_t af[2][FM], bf[2][FN];
-  auto read_frags = [&](const char* st) __attribute__((always_inline)) {
+  auto read_frags = [&](const char* ast, const char* bst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      af[0][i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 16 * ROWB + ch0);
-      af[1][i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 16 * ROWB + ch1);
+      af[0][i] = *reinterpret_cast<const bf16x8_t*>(ast + a_off + i * 16 * ROWB + ch0);
+      af[1][i] = *reinterpret_cast<const bf16x8_t*>(ast + a_off + i * 16 * ROWB + ch1);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      bf[0][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 16 * ROWB + ch0);
-      bf[1][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 16 * ROWB + ch1);
+      bf[0][j] = *reinterpret_cast<const bf16x8_t*>(bst + b_off + j * 16 * ROWB + ch0);
+      bf[1][j] = *reinterpret_cast<const bf16x8_t*>(bst + b_off + j * 16 * ROWB + ch1);
     }
   };
   auto mfma_step = [&](int ks) __attribute__((always_inline)) {
@@ -808,13 +800,11 @@ __global__ __launch_bounds__(512) void gemm_swiglu_pp_kernel(GemmArgs g) {
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bf[ks][j], acc[i][j], 0, 0, 0);
   };
-  // group 1: the tile's MFMAs with the weight copies of tile ktc issued between
-  // those of the second k-step (masks: 0x8 MFMA, 0x20 vector memory read)
-  auto mfma_copy = [&](int ktc, char* st) __attribute__((always_inline)) {
+  auto mfma_copy = [&](int ktc, int slot) __attribute__((always_inline)) {
     mfma_step(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < B_PW; ++j) copy(ktc, st, j);
+    for (int j = 0; j < B_PW; ++j) b_copy(ktc, slot, j);
     mfma_step(1);
 #pragma unroll
     for (int j = 0; j < B_PW; ++j) {
@@ -825,35 +815,41 @@ __global__ __launch_bounds__(512) void gemm_swiglu_pp_kernel(GemmArgs g) {
   };
   auto bar = []() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
 
-  // prologue: tiles 0 and 1 in flight, each group its own part; wait for tile 0
-  copy_tile(0, smem);
-  if (nk > 1) {
-    copy_tile(1, smem + STAGE);
-    if (grp == 0) __builtin_amdgcn_s_waitcnt(VmWait<A_PW>::imm);
-    else __builtin_amdgcn_s_waitcnt(VmWait<B_PW>::imm);
+  // prologue: activation tiles 0-1 and weight tiles 0-2 in flight (clamped to
+  // the last tile); wait for tile 0
+  if (grp == 0) {
+#pragma unroll
+    for (int j = 0; j < A_PW; ++j) a_copy(0, j);
+#pragma unroll
+    for (int j = 0; j < A_PW; ++j) a_copy(min(1, nk - 1), j);
+    __builtin_amdgcn_s_waitcnt(VmWait<A_PW>::imm);
   } else {
-    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int j = 0; j < B_PW; ++j) b_copy(min(s, nk - 1), s, j);
+    __builtin_amdgcn_s_waitcnt(VmWait<2 * B_PW>::imm);
   }
   lds_barrier();
 
-  // stage P holds the tiles of parity P; the loops run two tiles per
-  // iteration so that every stage address is a constant offset
   if (grp == 0) {
+    int slot = 0;
     auto step = [&](int kt, auto par) __attribute__((always_inline)) {
       constexpr int P = decltype(par)::value;
-      // phase 2kt: activations of tile kt+1 (its stage was freed by phase
-      // 2kt-1; tile 1 came with the prologue), then the fragments of tile kt
-      if (kt >= 1 && kt + 1 < nk) copy_tile(kt + 1, smem + (P ^ 1) * STAGE);
-      read_frags(smem + P * STAGE);
+      if (kt >= 1 && kt + 1 < nk) {
+#pragma unroll
+        for (int j = 0; j < A_PW; ++j) a_copy(kt + 1, j);
+      }
+      read_frags(smem + P * A_BYTES, smem + B_BASE + slot * B_BYTES);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // phase 2kt+1: the MFMAs of tile kt
       mfma_step(0);
       mfma_step(1);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wavefront's copies of tile kt+1
       bar();
       __builtin_amdgcn_sched_barrier(0);
+      slot = slot == 2 ? 0 : slot + 1;
     };
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
@@ -862,21 +858,21 @@ __global__ __launch_bounds__(512) void gemm_swiglu_pp_kernel(GemmArgs g) {
     }
     if (kt < nk) step(kt, IntC<0>{});
   } else {
-    lds_barrier();   // phase 0: group 0 reads tile 0
+    lds_barrier();
+    int slot = 0;
     auto step = [&](int kt, auto par) __attribute__((always_inline)) {
       constexpr int P = decltype(par)::value;
-      // phase 2kt+1: the fragments of tile kt; this wavefront's weight copies
-      // of tile kt+1 must have landed before the barrier
-      read_frags(smem + P * STAGE);
-      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+      read_frags(smem + P * A_BYTES, smem + B_BASE + slot * B_BYTES);
+      // this wavefront's weight copies of tile kt+1 (those of tile kt+2 may stay in flight)
+      __builtin_amdgcn_s_waitcnt(VmWait<B_PW>::imm);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // phase 2kt+2: the MFMAs of tile kt, with the weights of tile kt+2
-      // copied into tile kt's stage between them
-      mfma_copy(min(kt + 2, nk - 1), smem + P * STAGE);
+      // tile kt's ring slot is free: weights of tile kt+3 go there
+      mfma_copy(min(kt + 3, nk - 1), slot);
       __builtin_amdgcn_sched_barrier(0);
       if (kt + 1 < nk) bar();
       __builtin_amdgcn_sched_barrier(0);
+      slot = slot == 2 ? 0 : slot + 1;
     };
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
@@ -887,9 +883,6 @@ __global__ __launch_bounds__(512) void gemm_swiglu_pp_kernel(GemmArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // no copy may land after the block ends
 
-  // epilogue (as in gemm_swiglu_kernel): the low half of each 16-lane row
-  // finishes row 2q, the high half row 2q+1; a rotate by eight lanes brings
-  // each the value it is missing
   uint16_t* out = static_cast<uint16_t*>(g.out);
   const bool lo = l16 < 8;
 #pragma unroll
@@ -916,22 +909,31 @@ __global__ __launch_bounds__(512) void gemm_swiglu_pp_kernel(GemmArgs g) {
 // per SIMD).  The tiles (256 token rows x BN weight rows, 64-wide K tiles, eight
 // wavefronts of 32x32x16 MFMAs), swizzle, K slices and epilogues of
 // gemm_bf16_dma_kernel with the copy schedule of gemm_swiglu_pp_kernel:
-// waves 0-3 (token rows 0-127) copy the activation tile at the start of
-// their read phases, waves 4-7 (rows 128-255) copy the weight tile between
-// the MFMAs of the second half of their tile.
-template <int BN, int WM, int WN, int EPI, bool OUT_F32>
+// waves 0-3 (token rows 0-127) copy activation tiles at the start of their
+// read phases, waves 4-7 (rows 128-255) copy weight tiles between the MFMAs of
+// the second half of their tile.  The activation and weight tiles sit in rings
+// of SA and SB stages (two or three each, as the LDS allows): activation tile
+// kt+SA-1 goes into the stage of tile kt-1 when group 0 starts tile kt,
+// weight tile kt+SB into the stage of tile kt once group 1 has read it, so a
+// copy has up to two tiles of time to land before it is read.  Past the last
+// tile the copies repeat the last tile into a stage nobody reads any more (a
+// branch around them would split the scheduled MFMA block); each group waits
+// for its copies of tile kt+1 before the barrier that ends tile kt, and for
+// all of them before the epilogue.
+template <int BN, int WM, int WN, int EPI, bool OUT_F32, int SA = 2, int SB = 2>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_pp_dma_kernel(GemmArgs g) {
   constexpr int BM = 256, BK = 64, ROWB = BK * 2;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
-  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int B_BASE = SA * A_BYTES;
   constexpr int A_PW = A_BYTES / 1024 / 4, B_PW = B_BYTES / 1024 / 4;
-  constexpr int HALF = 2 * FM * FN;                         // MFMAs of two k-steps
+  constexpr int HALF = 2 * FM * FN;
   static_assert(WM * WN == 8 && TM * 2 * (WM / 2) == BM, "waves 0-3 cover token rows 0-127");
   static_assert(B_BYTES % 4096 == 0 && B_PW <= HALF, "copy split");
+  static_assert(SA >= 2 && SA <= 3 && SB >= 2 && SB <= 3, "ring depth");
   static_assert(EPI != 2 || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[SA * A_BYTES + SB * B_BYTES];
 
   const int wi = xcd_tile(blockIdx.x, gridDim.x);
   const int split = wi % g.splits, t = wi / g.splits;
@@ -945,9 +947,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_pp_dma_kernel(GemmArgs g) {
   const int grp = wave >> 2, cw = wave & 3;
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lh = lane >> 5;
-  // weight row of B-tile row r (SwiGLU: each wavefront column holds TN/2 gate
-  // rows then the TN/2 up rows of the same output columns); rows past N are
-  // clamped, their products land in discarded outputs
   auto b_row = [&](int r) -> int {
     if constexpr (EPI == 2) {
       const int w = r / TN, rr = r % TN;
@@ -972,19 +971,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_pp_dma_kernel(GemmArgs g) {
     }
   }
   const i32x4_t c_rsrc = grp == 0 ? buffer_rsrc(g.A, g.a_bytes) : buffer_rsrc(g.W, g.w_bytes);
-  const int c_lds = grp == 0 ? cw * A_PW * 1024 : A_BYTES + cw * B_PW * 1024;
-  auto kbyte = [&](int kt) { return __builtin_amdgcn_readfirstlane((k_begin + kt * BK) * 2); };
-  auto copy = [&](int kt, char* st, int j) __attribute__((always_inline)) {
-    dma16_buf(c_rsrc, c_src[j], kbyte(kt), st + c_lds + j * 1024);
+  auto kbyte = [&](int kt) { return __builtin_amdgcn_readfirstlane((k_begin + min(kt, nk - 1) * BK) * 2); };
+  auto a_copy = [&](int kt, int slot, int j) __attribute__((always_inline)) {
+    dma16_buf(c_rsrc, c_src[j], kbyte(kt), smem + slot * A_BYTES + (cw * A_PW + j) * 1024);
   };
-  auto copy_tile = [&](int kt, char* st) __attribute__((always_inline)) {
-    if (grp == 0) {
-#pragma unroll
-      for (int j = 0; j < A_PW; ++j) copy(kt, st, j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < B_PW; ++j) copy(kt, st, j);
-    }
+  auto b_copy = [&](int kt, int slot, int j) __attribute__((always_inline)) {
+    dma16_buf(c_rsrc, c_src[j], kbyte(kt), smem + B_BASE + slot * B_BYTES + (cw * B_PW + j) * 1024);
   };
 
   f32x16_t acc[FM][FN];
@@ -995,20 +987,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_pp_dma_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fragment rows are 32-aligned, so swz8(row) = swz8(lr)
   const int sw = swz8(lr);
-  const int a_off = (wm * TM + lr) * ROWB, b_off = A_BYTES + (wn * TN + lr) * ROWB;
+  const int a_off = (wm * TM + lr) * ROWB, b_off = (wn * TN + lr) * ROWB;
   bf16x8_t af[4][FM], bf[4][FN];
-  auto read_frags = [&](const char* st) __attribute__((always_inline)) {
+  auto read_frags = [&](const char* ast, const char* bst) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int ch = ((kk * 2 + lh) ^ sw) << 4;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[kk][i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 32 * ROWB + ch);
+        af[kk][i] = *reinterpret_cast<const bf16x8_t*>(ast + a_off + i * 32 * ROWB + ch);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bf[kk][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * ROWB + ch);
+        bf[kk][j] = *reinterpret_cast<const bf16x8_t*>(bst + b_off + j * 32 * ROWB + ch);
     }
   };
   auto mfma_steps = [&](int k0) __attribute__((always_inline)) {
@@ -1020,13 +1011,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_pp_dma_kernel(GemmArgs g) {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bf[kk][j], acc[i][j], 0, 0, 0);
   };
-  // group 1: the weight copies of tile ktc spread over the MFMAs of k-steps
-  // 2 and 3 (masks: 0x8 MFMA, 0x20 vector memory read)
-  auto mfma_copy = [&](int ktc, char* st) __attribute__((always_inline)) {
+  auto mfma_copy = [&](int ktc, int slot) __attribute__((always_inline)) {
     mfma_steps(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < B_PW; ++j) copy(ktc, st, j);
+    for (int j = 0; j < B_PW; ++j) b_copy(ktc, slot, j);
     mfma_steps(2);
     constexpr int EVERY = HALF / B_PW;
 #pragma unroll
@@ -1039,55 +1028,59 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_pp_dma_kernel(GemmArgs g) {
   };
   auto bar = []() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
 
-  copy_tile(0, smem);
-  if (nk > 1) {
-    copy_tile(1, smem + STAGE);
-    if (grp == 0) __builtin_amdgcn_s_waitcnt(VmWait<A_PW>::imm);
-    else __builtin_amdgcn_s_waitcnt(VmWait<B_PW>::imm);
+  // prologue: activation tiles 0 .. SA-2 and weight tiles 0 .. SB-1 in flight
+  // (clamped to the last tile); wait for tile 0
+  if (grp == 0) {
+#pragma unroll
+    for (int s = 0; s < SA - 1; ++s)
+#pragma unroll
+      for (int j = 0; j < A_PW; ++j) a_copy(s, s, j);
+    __builtin_amdgcn_s_waitcnt(VmWait<(SA - 2) * A_PW>::imm);
   } else {
-    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+#pragma unroll
+    for (int s = 0; s < SB; ++s)
+#pragma unroll
+      for (int j = 0; j < B_PW; ++j) b_copy(s, s, j);
+    __builtin_amdgcn_s_waitcnt(VmWait<(SB - 1) * B_PW>::imm);
   }
   lds_barrier();
 
+  int sa = 0, sb = 0;   // ring stages of tile kt
   if (grp == 0) {
-    auto step = [&](int kt, auto par) __attribute__((always_inline)) {
-      constexpr int P = decltype(par)::value;
-      if (kt >= 1 && kt + 1 < nk) copy_tile(kt + 1, smem + (P ^ 1) * STAGE);
-      read_frags(smem + P * STAGE);
+    for (int kt = 0; kt < nk; ++kt) {
+      // activations of tile kt+SA-1 into the stage of tile kt-1
+      const int fa = sa == 0 ? SA - 1 : sa - 1;
+#pragma unroll
+      for (int j = 0; j < A_PW; ++j) a_copy(kt + SA - 1, fa, j);
+      read_frags(smem + sa * A_BYTES, smem + B_BASE + sb * B_BYTES);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
       mfma_steps(0);
       mfma_steps(2);
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+      // this wavefront's copies of tile kt+1
+      __builtin_amdgcn_s_waitcnt(VmWait<(SA - 2) * A_PW>::imm);
       bar();
       __builtin_amdgcn_sched_barrier(0);
-    };
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, IntC<0>{});
-      step(kt + 1, IntC<1>{});
+      sa = sa == SA - 1 ? 0 : sa + 1;
+      sb = sb == SB - 1 ? 0 : sb + 1;
     }
-    if (kt < nk) step(kt, IntC<0>{});
   } else {
     lds_barrier();
-    auto step = [&](int kt, auto par) __attribute__((always_inline)) {
-      constexpr int P = decltype(par)::value;
-      read_frags(smem + P * STAGE);
-      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+    for (int kt = 0; kt < nk; ++kt) {
+      read_frags(smem + sa * A_BYTES, smem + B_BASE + sb * B_BYTES);
+      // this wavefront's weight copies of tile kt+1
+      __builtin_amdgcn_s_waitcnt(VmWait<(SB - 2) * B_PW>::imm);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      mfma_copy(min(kt + 2, nk - 1), smem + P * STAGE);
+      // tile kt's weight stage is free: weights of tile kt+SB go there
+      mfma_copy(kt + SB, sb);
       __builtin_amdgcn_sched_barrier(0);
       if (kt + 1 < nk) bar();
       __builtin_amdgcn_sched_barrier(0);
-    };
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, IntC<0>{});
-      step(kt + 1, IntC<1>{});
+      sa = sa == SA - 1 ? 0 : sa + 1;
+      sb = sb == SB - 1 ? 0 : sb + 1;
     }
-    if (kt < nk) step(kt, IntC<0>{});
   }
   __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // no copy may land after the block ends
 
@@ -1453,10 +1446,12 @@ static hipError_t run_partial_narrow(GemmArgs g, int splits, hipStream_t s) {
   const int blocks = g.m_tiles * g.n_tiles * g.splits;
   if constexpr (!SIGN1) {
     if (buffer_extents(g, static_cast<size_t>(g.N))) {
+      // (rings measured at the 8B shape: a third weight stage helps both
+      // widths; a third activation stage fits, and helps, only beside 128)
       if constexpr (BN == 192)
-        gemm_pp_dma_kernel<192, 4, 2, 4, OUT_F32><<<blocks, 512, 0, s>>>(g);
+        gemm_pp_dma_kernel<192, 4, 2, 4, OUT_F32, 2, 3><<<blocks, 512, 0, s>>>(g);
       else
-        gemm_pp_dma_kernel<128, 2, 4, 4, OUT_F32><<<blocks, 512, 0, s>>>(g);
+        gemm_pp_dma_kernel<128, 4, 2, 4, OUT_F32, 3, 3><<<blocks, 512, 0, s>>>(g);
       return hipGetLastError();
     }
   }
