@@ -13,6 +13,14 @@
 // v_mfma_f32_32x32x16_bf16 (lane = query, 32 key scores per lane), runs the
 // online softmax in fp32 with exp2, and accumulates O^T = V^T P^T, taking P
 // straight from the score registers and V^T from transposing LDS reads.
+//
+// Short micro-batches over short histories (a grid of at most half as many
+// blocks as CUs) take a two-key-group form: a block holds half as many query
+// heads, and its wavefronts form two groups that run the same queries over
+// alternate key blocks, each with its own K/V ring; at the end the second
+// group passes its running max, weight sum and unnormalised output through
+// LDS and the first merges them.  Twice the blocks, half the longest chain of
+// key blocks.
 #include <type_traits>
 
 #include "common.h"
@@ -72,7 +80,7 @@ template <> struct AttnOps<true> {
   static __device__ __forceinline__ float sum2(uint32_t pair, float acc) { return dot2_f16_sum(pair, acc); }
 };
 
-template <int HD, int NW, bool SPLIT, bool KV16>
+template <int HD, int NW, bool SPLIT, bool KV16, bool KSPLIT = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs a) {
   typedef AttnOps<KV16> Ops;
   typedef typename Ops::V8 V8;
@@ -81,22 +89,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   constexpr int CH = ROWB / 16;          // 16-byte chunks per row
   constexpr int RPI = 1024 / ROWB;       // rows per DMA instruction
   constexpr int TILE = KB * ROWB;        // bytes of one K (or V) block
-  constexpr int PW = TILE / 1024 / NW;   // DMA instructions per wave per K (or V) block
+  constexpr int GW = KSPLIT ? NW / 2 : NW;   // wavefronts per key group
+  constexpr int PW = TILE / 1024 / GW;   // DMA instructions per wave per K (or V) block
   constexpr int KS = HD / 16;            // k-steps of the QK^T contraction
   constexpr int DB = HD / 32;            // 32-wide blocks of the head dimension
   constexpr int RPL = 256 / ROWB;        // key rows per LDS bank line
   auto swz_k = [](int r) { return (r / RPL) & (CH - 1); };
   auto swz_v = [](int r) { return ((r / RPL) & (CH / 4 - 1)) * 4; };
-  constexpr int SK = 3, SV = 2;          // ring slots for K and V blocks
-  __shared__ __attribute__((aligned(1024))) char smem[(SK + SV) * TILE];
-  char* const kring = smem;
-  char* const vring = smem + SK * TILE;
+  constexpr int SK = KSPLIT ? 2 : 3, SV = 2;   // ring slots for K and V blocks (per key group)
+  constexpr int RING = (SK + SV) * TILE;
+  __shared__ __attribute__((aligned(1024))) char smem[(KSPLIT ? 2 : 1) * RING];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
+  // key group (two groups take alternate key blocks of the same queries) and
+  // wavefront within it
+  const int kg = KSPLIT ? wave / GW : 0, wq = KSPLIT ? wave % GW : wave;
+  char* const kring = smem + kg * RING;
+  char* const vring = kring + SK * TILE;
   const int lr = lane & 31, lh = lane >> 5;
   const int hpb = a.hpb;
-  const int tsub = NW / hpb;           // 32-token slices per block
+  const int tsub = GW / hpb;           // 32-token slices per block
   const int bt = 32 * tsub;            // tokens per block
   // Work item w = (kv head j, head quad, tile[, key range]), tile fastest
   // (after the key range) and longest rows first.  Blocks are dealt
@@ -112,8 +125,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   const int quads = a.group / hpb;
   const int jq = w / a.tiles;
   const int j = jq / quads, quad = jq % quads;
-  const int h = j * a.group + quad * hpb + wave % hpb;
-  const int t0w = tile * bt + (wave / hpb) * 32;      // first query token of this wave
+  const int h = j * a.group + quad * hpb + wq % hpb;
+  const int t0w = tile * bt + (wq / hpb) * 32;        // first query token of this wave
   const int t = t0w + lr;                             // this lane's query token
   const bool q_ok = t < a.M;
   const int pos = a.start + t;
@@ -146,6 +159,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   const int per = (nkb + n_split - 1) / n_split;
   const int kb_lo = split * per;
   const int kb_hi = min(nkb, kb_lo + per);
+  // step i of this wavefront's key group works on key block kb_lo + kg + KSTEP*i;
+  // with two groups the second one's last step may be the block past the
+  // last, whose keys are all masked
+  constexpr int KSTEP = KSPLIT ? 2 : 1;
+  const int n_steps = (kb_hi - kb_lo + KSTEP - 1) / KSTEP;
+  auto kb_of = [&](int i) { return kb_lo + kg + KSTEP * i; };
   const uint16_t* kbase = a.k + static_cast<size_t>(j) * a.max_seq * HD;
   const uint16_t* vbase = a.v + static_cast<size_t>(j) * a.max_seq * HD;
 
@@ -158,23 +177,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   uint32_t k_off[PW], v_off[PW];
 #pragma unroll
   for (int jj = 0; jj < PW; ++jj) {
-    const int row = (wave * PW + jj) * RPI + d_row;
+    const int row = (wq * PW + jj) * RPI + d_row;
     k_off[jj] = row * ROWB + (d_slot ^ swz_k(row)) * 16;
     v_off[jj] = row * ROWB + (d_slot ^ swz_v(row)) * 16;
   }
   const int full_blocks = kv_end / KB;
-  auto issue = [&](int kb, bool is_v) __attribute__((always_inline)) {
-    char* st = is_v ? vring + (kb % SV) * TILE : kring + (kb % SK) * TILE;
+  auto issue = [&](int i, bool is_v) __attribute__((always_inline)) {
+    const int kb = kb_of(i);
+    char* st = is_v ? vring + (i % SV) * TILE : kring + (i % SK) * TILE;
     const uint16_t* base = is_v ? vbase : kbase;
     if (kb < full_blocks) {
       const char* blk = reinterpret_cast<const char*>(base) + static_cast<size_t>(kb) * TILE;
 #pragma unroll
       for (int jj = 0; jj < PW; ++jj)
-        dma16(blk + (is_v ? v_off[jj] : k_off[jj]), st + (wave * PW + jj) * 1024);
+        dma16(blk + (is_v ? v_off[jj] : k_off[jj]), st + (wq * PW + jj) * 1024);
     } else {
 #pragma unroll
       for (int jj = 0; jj < PW; ++jj) {
-        const int q = wave * PW + jj;
+        const int q = wq * PW + jj;
         const int row = q * RPI + d_row;
         const int key = min(kb * KB + row, kv_end - 1);
         const int sw = is_v ? swz_v(row) : swz_k(row);
@@ -185,8 +205,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
 
   // S^T of block kb for two 32-key halves: lane (query lr) gets keys
   // 8*(r/4) + 4*lh + r%4 of each half
-  auto scores = [&](int kb, f32x16_t (&sc)[2]) __attribute__((always_inline)) {
-    const char* Kt = kring + (kb % SK) * TILE;
+  auto scores = [&](int i, f32x16_t (&sc)[2]) __attribute__((always_inline)) {
+    const char* Kt = kring + (i % SK) * TILE;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
@@ -232,10 +252,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   }
 
   // prologue: K(lo), V(lo), K(lo+1) in flight; scores of block lo once K(lo) landed
-  issue(kb_lo, false);
-  issue(kb_lo, true);
-  if (kb_hi - kb_lo > 1) {
-    issue(kb_lo + 1, false);
+  issue(0, false);
+  issue(0, true);
+  if (n_steps > 1) {
+    issue(1, false);
     __builtin_amdgcn_s_waitcnt(VmWait<2 * PW>::imm);
   } else {
     __builtin_amdgcn_s_waitcnt(VmWait<PW>::imm);
@@ -244,12 +264,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   // One key block: softmax of block kb from its scores s, with the scores of
   // block kb+1 computed into s_next on the way.  The loop alternates the two
   // score arrays so that no registers are copied between blocks.
-  auto step = [&](int kb, f32x16_t (&s)[2], f32x16_t (&s_next)[2]) __attribute__((always_inline)) {
-    const int key0 = kb * KB;
-    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wave's copies of V(kb), K(kb+1)
-    lds_barrier();   // everyone's; V slot of kb-1 and K slot of kb-1 are free
-    if (kb + 1 < kb_hi) issue(kb + 1, true);
-    if (kb + 2 < kb_hi) issue(kb + 2, false);
+  auto step = [&](int i, f32x16_t (&s)[2], f32x16_t (&s_next)[2]) __attribute__((always_inline)) {
+    const int key0 = kb_of(i) * KB;
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wave's copies of V(i), K(i+1)
+    lds_barrier();   // everyone's; the V and K slots of step i-1 are free
+    if (i + 1 < n_steps) issue(i + 1, true);
+    if (i + 2 < n_steps) issue(i + 2, false);
     // the causal mask only cuts blocks that reach past the wave's first query
     if (key0 + KB - 1 > pos_lo) {
 #pragma unroll
@@ -273,7 +293,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
       // key has seen no key yet (m_run = m_blk = -inf) while another lane of
       // the wavefront raised the ballot: exp2(-inf - -inf) would be NaN, and
       // its o and l (still zero) need no rescale.
-      const float alpha = SPLIT && m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      const float alpha = (SPLIT || KSPLIT) && m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
 #pragma unroll
@@ -288,7 +308,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
     // scheduling fences keep the groups in that order (the compiler places
     // the LDS waits).  The last iteration recomputes its own block, whose K
     // slot is still intact.
-    const char* Kt = kring + (min(kb + 1, kb_hi - 1) % SK) * TILE;
+    const char* Kt = kring + (min(i + 1, n_steps - 1) % SK) * TILE;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -304,7 +324,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
 #pragma unroll
     for (int i = 0; i < AK; ++i) kf[i] = kread(i);
     // (a key range of the split form may hide every key from a row so far)
-    const float neg_m = SPLIT && m_run == -INFINITY ? 0.f : -m_run;
+    const float neg_m = (SPLIT || KSPLIT) && m_run == -INFINITY ? 0.f : -m_run;
     V8 pf[4];   // B operand of step 2*hb + half: slots (lh, e) <- r = 8*half + e
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -324,7 +344,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
     // each run of four consecutive keys is one transposing read.  Product j
     // takes head-dim block j % DB (independent chains) and step j / DB; its
     // V^T fragment is read AV products ahead.
-    const char* Vt = vring + (kb % SV) * TILE;
+    const char* Vt = vring + (i % SV) * TILE;
     auto vread = [&](int jj) __attribute__((always_inline)) {
       const int dim = (jj % DB) * 32 + tr_dim, st = jj / DB;
       const int r0 = (st >> 1) * 32 + (st & 1) * 16 + lh * 4 + tr_key, r1 = r0 + 8;
@@ -359,15 +379,51 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   };
 
   f32x16_t sa[2], sb[2];
-  scores(kb_lo, sa);
-  int kb = kb_lo;
-  for (; kb + 1 < kb_hi; kb += 2) {
-    step(kb, sa, sb);
-    step(kb + 1, sb, sa);
+  scores(0, sa);
+  int i = 0;
+  for (; i + 1 < n_steps; i += 2) {
+    step(i, sa, sb);
+    step(i + 1, sb, sa);
   }
-  if (kb < kb_hi) step(kb, sa, sb);
+  if (i < n_steps) step(i, sa, sb);
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if constexpr (KSPLIT) {
+    // Group 1 hands its reference max, weight sum and unnormalised output to
+    // group 0, which rescales both to the larger max and adds them.  Group 0
+    // always holds key 0, visible to every row, so its max is finite; a row
+    // that saw no key of group 1's blocks has max -inf there and weight 0.
+    float4* xo = reinterpret_cast<float4*>(smem);   // [DB*4][GW*64 lanes] float4
+    float* xm = reinterpret_cast<float*>(smem) + DB * 16 * GW * 64;
+    const int me = wq * 64 + lane;
+    lds_barrier();   // every wavefront is done with the rings
+    if (kg == 1) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          xo[(d * 4 + r4) * GW * 64 + me] = make_float4(o[d][r4 * 4 + 0], o[d][r4 * 4 + 1],
+                                                        o[d][r4 * 4 + 2], o[d][r4 * 4 + 3]);
+      xm[me] = m_run;
+      xm[GW * 64 + me] = l_tot;
+    }
+    lds_barrier();
+    if (kg == 1) return;
+    const float m1 = xm[me], l1 = xm[GW * 64 + me];
+    const float mm = fmaxf(m_run, m1);
+    const float f0 = fast_exp2(m_run - mm), f1 = fast_exp2(m1 - mm);
+    l_tot = l_tot * f0 + l1 * f1;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 v = xo[(d * 4 + r4) * GW * 64 + me];
+        o[d][r4 * 4 + 0] = o[d][r4 * 4 + 0] * f0 + v.x * f1;
+        o[d][r4 * 4 + 1] = o[d][r4 * 4 + 1] * f0 + v.y * f1;
+        o[d][r4 * 4 + 2] = o[d][r4 * 4 + 2] * f0 + v.z * f1;
+        o[d][r4 * 4 + 3] = o[d][r4 * 4 + 3] * f0 + v.w * f1;
+      }
+  }
   if (!q_ok) return;
   if constexpr (SPLIT) {
     const size_t pr = (static_cast<size_t>(split) * a.M + t) * a.nq + h;
@@ -643,9 +699,16 @@ hipError_t launch_attention(Act act, bool kv16, const void* q, int q_ld, const v
     }
     return hipGetLastError();
   }
-  dim3 grid(gr.blocks);
+  // A grid that leaves at least half of the CUs idle (short micro-batches
+  // over short histories) takes the two-key-group form: each block holds half
+  // as many query heads in two wavefront groups that split the key blocks, so
+  // there are twice the blocks and the longest chain of key blocks is halved.
+  const bool ksplit = gr.waves == 4 && gr.blocks * 2 <= 256 && gr.hpb % 2 == 0;
+  if (ksplit) a.hpb = gr.hpb / 2;
+  dim3 grid(ksplit ? gr.blocks * 2 : gr.blocks);
 #define TLP_ATTN(HD_, KV_)                                                                  \
-  if (a.waves == 8) attn_fwd_bf16_kernel<HD_, 8, false, KV_><<<grid, 512, 0, s>>>(a);       \
+  if (ksplit) attn_fwd_bf16_kernel<HD_, 4, false, KV_, true><<<grid, 256, 0, s>>>(a);       \
+  else if (a.waves == 8) attn_fwd_bf16_kernel<HD_, 8, false, KV_><<<grid, 512, 0, s>>>(a);  \
   else attn_fwd_bf16_kernel<HD_, 4, false, KV_><<<grid, 256, 0, s>>>(a);
   if (head_dim == 128) {
     if (kv16) { TLP_ATTN(128, true) } else { TLP_ATTN(128, false) }
