@@ -1387,8 +1387,8 @@ static int big_tiles(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256
 // Split-K plan of the Partial epilogue: tile width (256 or 128 columns, 256
 // rows either way) and slice count, about one work item per CU.  The next row
 // pass reads every slice once, so 256x128 tiles with half as many slices are
-// used where that pays: the output projection at the 8B shape (4 slices of
-// 256x128 instead of 8 of 256x256).
+// used where that pays: the output and down projections at the 8B shape (4
+// slices of 256x128 instead of 8 of 256x256).
 struct PartialPlan {
   int bn, splits;
 };
@@ -1408,10 +1408,10 @@ static PartialPlan partial_plan(int M, int N, int K, bool narrow_ok) {
   }
   const int narrow = ((M + 255) / 256) * ((N + 127) / 128);
   int splits = kCUs / narrow;
-  // (measured: with fewer than 4 slices the narrow grid under-fills the GPU,
-  // and beyond K = 4096 its extra weight traffic per flop outweighs the
-  // slices it saves)
-  if (narrow_ok && splits >= 4 && K <= 4096)
+  // (measured: with fewer than 4 slices the narrow grid under-fills the GPU;
+  // at K = 14336 of the 8B down projection 4 slices of 256x128 tiles beat 8
+  // of 256x256 by the slices the next row pass no longer reads)
+  if (narrow_ok && splits >= 4)
     return {128, clamp(splits > kMaxSplits ? kMaxSplits : splits)};
   splits = kCUs / big_tiles(M, N);   // the grid stays within one wave of work items
   if (splits > kMaxSplits) splits = kMaxSplits;
