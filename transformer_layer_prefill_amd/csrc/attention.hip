@@ -51,7 +51,9 @@ struct AttnArgs {
 // K and V blocks of 64 keys are copied global -> LDS with DMA into rings of
 // three K and two V slots: while block kb's softmax runs on the VALUs, the
 // MFMAs already compute block kb+1's scores, and the copies of K(kb+2) and
-// V(kb+1) are in flight.
+// V(kb+1) are in flight.  Eight wavefronts (one block per CU) use four K and
+// four V slots and meet at a barrier every second key block, the copies of
+// the next pair of blocks in flight meanwhile.
 // Rows are stored as 16-byte chunks, chunk c of key row r at slot c ^ swz(r).
 // The LDS has 64 banks (256 bytes per cycle): a b128 read is served 16 lanes
 // at a time, a transposing b64 read 32 lanes at a time.  With RPL = 256 /
@@ -80,6 +82,22 @@ template <> struct AttnOps<true> {
   static __device__ __forceinline__ float sum2(uint32_t pair, float acc) { return dot2_f16_sum(pair, acc); }
 };
 
+
+// Global -> LDS copy of 16 bytes per lane (lane l writes lds + 16 l) issued
+// from an asm block.  The compiler's wait insertion cannot tell which ring
+// slot a copy writes, so a copy it tracks makes it drain every LDS read and
+// every copy before the next LDS read; the kernel orders its copies and
+// reads itself (its own vmcnt waits and barriers), so these are left
+// untracked.  `lds` must be wavefront-uniform (it goes to M0).
+__device__ __forceinline__ void dma16_untracked(const void* src, void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(src)
+               : "memory", "m0");
+}
+
 template <int HD, int NW, bool SPLIT, bool KV16, bool KSPLIT = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs a) {
   typedef AttnOps<KV16> Ops;
@@ -96,7 +114,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   constexpr int RPL = 256 / ROWB;        // key rows per LDS bank line
   auto swz_k = [](int r) { return (r / RPL) & (CH - 1); };
   auto swz_v = [](int r) { return ((r / RPL) & (CH / 4 - 1)) * 4; };
-  constexpr int SK = KSPLIT ? 2 : 3, SV = 2;   // ring slots for K and V blocks (per key group)
+  // Eight wavefronts (one block per CU) meet at a barrier every second key
+  // block, with four K and four V ring slots, so the copies of a pair of
+  // blocks are issued a whole pair ahead.
+  constexpr bool PAIR = NW == 8 && !KSPLIT && !SPLIT;
+  constexpr int SK = PAIR ? 4 : KSPLIT ? 2 : 3, SV = PAIR ? 4 : 2;   // ring slots (per key group)
   constexpr int RING = (SK + SV) * TILE;
   __shared__ __attribute__((aligned(1024))) char smem[(KSPLIT ? 2 : 1) * RING];
 
@@ -190,7 +212,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
       const char* blk = reinterpret_cast<const char*>(base) + static_cast<size_t>(kb) * TILE;
 #pragma unroll
       for (int jj = 0; jj < PW; ++jj)
-        dma16(blk + (is_v ? v_off[jj] : k_off[jj]), st + (wq * PW + jj) * 1024);
+        dma16_untracked(blk + (is_v ? v_off[jj] : k_off[jj]), st + (wq * PW + jj) * 1024);
     } else {
 #pragma unroll
       for (int jj = 0; jj < PW; ++jj) {
@@ -198,7 +220,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
         const int row = q * RPI + d_row;
         const int key = min(kb * KB + row, kv_end - 1);
         const int sw = is_v ? swz_v(row) : swz_k(row);
-        dma16(base + static_cast<size_t>(key) * HD + (d_slot ^ sw) * 8, st + q * 1024);
+        dma16_untracked(base + static_cast<size_t>(key) * HD + (d_slot ^ sw) * 8, st + q * 1024);
       }
     }
   };
@@ -251,10 +273,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
     return;
   }
 
-  // prologue: K(lo), V(lo), K(lo+1) in flight; scores of block lo once K(lo) landed
+  // prologue: K(lo), V(lo), K(lo+1) in flight; scores of block lo once K(lo)
+  // landed.  Paired: K(0..2) and V(0..1), everything landed.
   issue(0, false);
   issue(0, true);
-  if (n_steps > 1) {
+  if constexpr (PAIR) {
+    if (n_steps > 1) {
+      issue(1, false);
+      issue(1, true);
+    }
+    if (n_steps > 2) issue(2, false);
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+  } else if (n_steps > 1) {
     issue(1, false);
     __builtin_amdgcn_s_waitcnt(VmWait<2 * PW>::imm);
   } else {
@@ -264,12 +294,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   // One key block: softmax of block kb from its scores s, with the scores of
   // block kb+1 computed into s_next on the way.  The loop alternates the two
   // score arrays so that no registers are copied between blocks.
-  auto step = [&](int i, f32x16_t (&s)[2], f32x16_t (&s_next)[2]) __attribute__((always_inline)) {
+  auto step = [&](int i, f32x16_t (&s)[2], f32x16_t (&s_next)[2], bool sync) __attribute__((always_inline)) {
     const int key0 = kb_of(i) * KB;
-    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wave's copies of V(i), K(i+1)
-    lds_barrier();   // everyone's; the V and K slots of step i-1 are free
-    if (i + 1 < n_steps) issue(i + 1, true);
-    if (i + 2 < n_steps) issue(i + 2, false);
+    if constexpr (PAIR) {
+      // at an even step: this wave's copies of V(i), V(i+1), K(i+1), K(i+2)
+      // landed, then everyone's; the slots of steps i-2 and i-1 are free
+      if (sync) {
+        __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+        lds_barrier();
+        if (i + 2 < n_steps) issue(i + 2, true);
+        if (i + 3 < n_steps) {
+          issue(i + 3, true);
+          issue(i + 3, false);
+        }
+        if (i + 4 < n_steps) issue(i + 4, false);
+      }
+    } else {
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // this wave's copies of V(i), K(i+1)
+      lds_barrier();   // everyone's; the V and K slots of step i-1 are free
+      if (i + 1 < n_steps) issue(i + 1, true);
+      if (i + 2 < n_steps) issue(i + 2, false);
+    }
     // the causal mask only cuts blocks that reach past the wave's first query
     if (key0 + KB - 1 > pos_lo) {
 #pragma unroll
@@ -382,10 +427,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(AttnArgs
   scores(0, sa);
   int i = 0;
   for (; i + 1 < n_steps; i += 2) {
-    step(i, sa, sb);
-    step(i + 1, sb, sa);
+    step(i, sa, sb, true);
+    step(i + 1, sb, sa, !PAIR);
   }
-  if (i < n_steps) step(i, sa, sb);
+  if (i < n_steps) step(i, sa, sb, true);
+  __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // (every copy has landed: the last steps issue none)
 
   float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if constexpr (KSPLIT) {
