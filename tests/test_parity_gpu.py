@@ -110,6 +110,13 @@ SMALL = [
            n_tokens=2000, start=37, max_seq=2048),
     _small("bf16-8wave-g4-ragged", hidden=256, inter=512, nq=32, nkv=8, head_dim=128,
            n_tokens=1990, start=0, max_seq=2048),
+    # QKV products whose 128-row tiles fill the GPU in one pass (bf16 rows, no
+    # K slices): 4 x 64 tiles of 96 columns over 450 rows, and 3 x 64 tiles of
+    # 64 columns over 300 rows (ragged last tile in both)
+    _small("bf16-qkv-stream96-ragged", hidden=256, inter=512, nq=32, nkv=8, head_dim=128,
+           n_tokens=450, start=3, max_seq=512),
+    _small("bf16-qkv-stream64-ragged", hidden=512, inter=512, nq=32, nkv=16, head_dim=64,
+           n_tokens=300, start=5, max_seq=320),
 ]
 
 

@@ -1251,6 +1251,158 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_spread_kernel(GemmArgs g
   gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh, split);
 }
 
+// ---- projections of few token rows: 128-row tiles over the whole of K -------
+// For a bf16 product whose 128-row tiles fill the CUs without splitting K
+// (the QKV projection of a 512-token micro-batch: 4 x 64 tiles of 128x96).
+// A block owns 128 token rows x BN weight rows over all of K, so it writes
+// finished bf16 rows and no fp32 partial slices go through memory (the row
+// pass that follows reads 2 bytes per element instead of the 4 x 4 of four
+// slices).  Such a tile needs more operand bytes per flop than the big tiles,
+// so the kernel is built to stream them: NS stages of 64-wide K tiles in a
+// ring, refilled by global->LDS buffer copies NS tiles ahead, and the four
+// wavefronts (4x1 or 2x2 of 32x32x16 MFMA fragments) read a whole tile's
+// fragments into registers while the MFMAs of the previous tile run.
+// Scheduling pattern: copy j (of C) follows MFMAs ((j+1)*N)/C - (j*N)/C of a
+// run of N (masks: 0x8 MFMA, 0x20 vector memory read).
+template <int J, int N, int C>
+struct SpreadCopies {
+  static __device__ __forceinline__ void place() {
+    constexpr int m = ((J + 1) * N) / C - (J * N) / C;
+    if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    SpreadCopies<J + 1, N, C>::place();
+  }
+};
+template <int N, int C>
+struct SpreadCopies<C, N, C> {
+  static __device__ __forceinline__ void place() {}
+};
+
+template <int BN, int WM, int WN, int EPI, bool OUT_F32, int NS>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
+  constexpr int BM = 128, BK = 64, ROWB = 128;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_PW = A_BYTES / 1024 / 4, B_PW = B_BYTES / 1024 / 4;
+  constexpr int CPW = A_PW + B_PW;
+  static_assert(WM * WN == 4 && FM * 32 == TM && FN * 32 == TN, "four wavefronts of 32x32 fragments");
+  static_assert(A_PW * 4096 == A_BYTES && B_PW * 4096 == B_BYTES, "copy split");
+  static_assert((NS - 2) * CPW <= 63 && NS >= 3, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+
+  const int wi = xcd_tile(blockIdx.x, gridDim.x);
+  const int mt = wi % g.m_tiles, nt = wi / g.m_tiles;
+  const int m0 = mt * BM;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int nk = g.K / BK;
+
+  // copy j < A_PW: activation block A_PW*wave + j; else weight block
+  // B_PW*wave + j - A_PW (1 KB = 8 rows of 128 bytes; lane l fetches chunk
+  // (l & 7) ^ swz8(row) of row l >> 3; rows past M or N re-fetch the last one)
+  const int drow = lane >> 3, dslot = lane & 7;
+  uint32_t c_src[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    if (j < A_PW) {
+      const int row = (A_PW * wave + j) * 8 + drow;
+      c_src[j] = (static_cast<uint32_t>(min(m0 + row, g.M - 1)) * g.lda + (dslot ^ swz8(row)) * 8) * 2;
+    } else {
+      const int row = (B_PW * wave + j - A_PW) * 8 + drow;
+      c_src[j] = (static_cast<uint32_t>(min(nt * BN + row, g.N - 1)) * g.K + (dslot ^ swz8(row)) * 8) * 2;
+    }
+  }
+  const i32x4_t a_rsrc = buffer_rsrc(g.A, g.a_bytes);
+  const i32x4_t b_rsrc = buffer_rsrc(g.W, g.w_bytes);
+  // tile kt (clamped to the last one) into ring stage `slot`
+  auto copy = [&](int kt, int slot, int j) __attribute__((always_inline)) {
+    const int kb = __builtin_amdgcn_readfirstlane(min(kt, nk - 1) * BK * 2);
+    char* st = smem + slot * STAGE;
+    if (j < A_PW) dma16_buf(a_rsrc, c_src[j], kb, st + (A_PW * wave + j) * 1024);
+    else dma16_buf(b_rsrc, c_src[j], kb, st + A_BYTES + (B_PW * wave + j - A_PW) * 1024);
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int sw = swz8(lr);
+  const int a_off = (wm * TM + lr) * ROWB, b_off = A_BYTES + (wn * TN + lr) * ROWB;
+  int ch[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) ch[kk] = ((kk * 2 + lh) ^ sw) << 4;
+  // all four k-steps of a tile's fragments, double-buffered across tiles
+  bf16x8_t ax[4][FM], bx[4][FN], ay[4][FM], by[4][FN];
+  auto frags = [&](bf16x8_t (&AF)[4][FM], bf16x8_t (&BF)[4][FN], const char* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        AF[kk][i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 32 * ROWB + ch[kk]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        BF[kk][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * ROWB + ch[kk]);
+    }
+  };
+  auto mma = [&](bf16x8_t (&AF)[4][FM], bf16x8_t (&BF)[4][FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AF[kk][i], BF[kk][j], acc[i][j], 0, 0, 0);
+  };
+
+  // prologue: tiles 0 .. NS-1 in flight; tiles 0 and 1 landed; everyone holds
+  // tile 0 in registers before its stage is refilled
+#pragma unroll
+  for (int t = 0; t < NS; ++t)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) copy(t, t, j);
+  __builtin_amdgcn_s_waitcnt(VmWait<(NS - 2) * CPW>::imm);
+  lds_barrier();
+  frags(ax, bx, smem);
+  lds_barrier();
+
+  // step kt: fragments of tile kt are in registers; read those of tile kt+1,
+  // run tile kt's MFMAs with the copies of tile kt+NS into tile kt's stage
+  // between them; wait for this wavefront's copies of tile kt+2, then the
+  // barrier (all reads of tile kt+1 done, every copy of tile kt+2 landed)
+  int slot = 0;   // ring stage of tile kt
+  auto step = [&](int kt, bf16x8_t (&AC)[4][FM], bf16x8_t (&BC)[4][FN], bf16x8_t (&AN)[4][FM],
+                  bf16x8_t (&BN_)[4][FN]) __attribute__((always_inline)) {
+    const int next = slot == NS - 1 ? 0 : slot + 1;
+    frags(AN, BN_, smem + next * STAGE);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) copy(kt + NS, slot, j);
+    mma(AC, BC);
+    // masks: 0x100 LDS read, 0x8 MFMA, 0x20 vector memory read
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * (FM + FN), 0);
+    SpreadCopies<0, 4 * FM * FN, CPW>::place();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(VmWait<(NS - 2) * CPW>::imm);
+    lds_barrier();
+    slot = next;
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, ax, bx, ay, by);
+    step(kt + 1, ay, by, ax, bx);
+  }
+  if (kt < nk) step(kt, ax, bx, ay, by);
+  __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);   // no copy may land after the block ends
+
+  gemm_epilogue<FM, FN, TM, TN, BN, EPI, OUT_F32>(g, acc, m0, nt, wm, wn, lr, lh, 0);
+}
+
 // ---- fp32 FMA kernel --------------------------------------------------------
 // 64x64 tile, 256 threads; thread (tx, ty) owns rows ty*4..+4 and columns
 // {2tx, 2tx+1, 32+2tx, 33+2tx}, so the SwiGLU epilogue finds gate column c
@@ -1495,6 +1647,27 @@ static hipError_t run_swiglu_narrow(GemmArgs g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 128-row stream tiles: 96 columns when N splits into them and 64-column
+// tiles would need more than one block per CU, else 64 columns.
+static bool stream_w96(int M, int N) {
+  const long mt = (M + 127) / 128;
+  return N % 96 == 0 && mt * (N / 96) <= kCUs && mt * ((N + 63) / 64) > kCUs;
+}
+static long stream_blocks(int M, int N) {
+  const long mt = (M + 127) / 128;
+  return mt * (stream_w96(M, N) ? N / 96 : (N + 63) / 64);
+}
+// A bf16 product takes the stream kernel when its 256x256 tiles would leave
+// a quarter of the CUs idle and its 128-row tiles fill more than half of
+// them in a single pass.
+static bool stream_fits(int M, int N, int K) {
+  if (K % 64 != 0 || M <= 0 || big_tiles(M, N) >= kCUs * 3 / 4) return false;
+  const long b = stream_blocks(M, N);
+  return b > kCUs / 2 && b <= kCUs;
+}
+
+bool gemm_store_direct(int M, int N, int K, bool sign1) { return !sign1 && stream_fits(M, N, K); }
+
 template <int EPI, bool SIGN1, bool OUT_F32>
 static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
   if constexpr (EPI == 2 && !OUT_F32) {
@@ -1511,6 +1684,21 @@ static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
     return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, p.splits, s);
   }
   if (tiles_big >= kCUs * 3 / 4) return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, 1, s);
+  if constexpr (EPI == 0 && !SIGN1) {
+    if (stream_fits(g.M, g.N, g.K) && buffer_extents(g, static_cast<size_t>(g.N))) {
+      g.m_tiles = (g.M + 127) / 128;
+      g.splits = 1;
+      g.k_split = g.K;
+      if (stream_w96(g.M, g.N)) {
+        g.n_tiles = g.N / 96;
+        gemm_stream_kernel<96, 4, 1, EPI, OUT_F32, 5><<<g.m_tiles * g.n_tiles, 256, 0, s>>>(g);
+      } else {
+        g.n_tiles = (g.N + 63) / 64;
+        gemm_stream_kernel<64, 2, 2, EPI, OUT_F32, 5><<<g.m_tiles * g.n_tiles, 256, 0, s>>>(g);
+      }
+      return hipGetLastError();
+    }
+  }
   return run_bf16<128, 128, 2, 2, EPI, SIGN1, OUT_F32>(g, 1, s);
 }
 
