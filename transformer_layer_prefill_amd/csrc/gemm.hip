@@ -1666,7 +1666,17 @@ static bool stream_fits(int M, int N, int K) {
   return b > kCUs / 2 && b <= kCUs;
 }
 
-bool gemm_store_direct(int M, int N, int K, bool sign1) { return !sign1 && stream_fits(M, N, K); }
+// ... or on 256x192 tiles when those alone fill the GPU (the split plan for
+// the product has a single slice: QKV at 2048 tokens).
+static bool store_pp192(int M, int N, int K) {
+  if (K % 64 != 0) return false;
+  const PartialPlan p = partial_plan(M, N, K, true);
+  return p.bn == 192 && p.splits == 1;
+}
+
+bool gemm_store_direct(int M, int N, int K, bool sign1) {
+  return !sign1 && (store_pp192(M, N, K) || stream_fits(M, N, K));
+}
 
 template <int EPI, bool SIGN1, bool OUT_F32>
 static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
@@ -1682,6 +1692,16 @@ static hipError_t pick_bf16(GemmArgs g, hipStream_t s) {
     if (p.bn == 128) return run_partial_narrow<128, OUT_F32, SIGN1>(g, p.splits, s);
     if (p.bn == 192) return run_partial_narrow<192, OUT_F32, SIGN1>(g, p.splits, s);
     return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, p.splits, s);
+  }
+  if constexpr (EPI == 0 && !SIGN1) {
+    if (store_pp192(g.M, g.N, g.K) && buffer_extents(g, static_cast<size_t>(g.N))) {
+      g.m_tiles = (g.M + 255) / 256;
+      g.n_tiles = g.N / 192;
+      g.splits = 1;
+      g.k_split = g.K;
+      gemm_pp_dma_kernel<192, 4, 2, EPI, OUT_F32, 2, 3><<<g.m_tiles * g.n_tiles, 512, 0, s>>>(g);
+      return hipGetLastError();
+    }
   }
   if (tiles_big >= kCUs * 3 / 4) return run_bf16<256, 256, 2, 4, EPI, SIGN1, OUT_F32>(g, 1, s);
   if constexpr (EPI == 0 && !SIGN1) {

@@ -58,9 +58,10 @@ hipError_t launch_gemm(const GemmCall& c, hipStream_t s);
 
 // K slices the Partial epilogue uses for an M x N x K bf16 product (1 if not split).
 int gemm_partial_splits(int M, int N, int K);
-// True when an M x N x K bf16 Store product runs in one pass on 128-row
-// tiles that fill the GPU (finished bf16 rows, no K slices): such a product
-// is better stored directly than split into fp32 slices.
+// True when an M x N x K bf16 Store product runs in one pass on tiles that
+// fill the GPU (128-row stream tiles, or 256x192 tiles that alone make a
+// wave of blocks): such a product is better stored directly as bf16 rows
+// than split into fp32 slices.
 bool gemm_store_direct(int M, int N, int K, bool sign1);
 
 // ---- skinny-M projection (decode steps, verify rows) -----------------------
