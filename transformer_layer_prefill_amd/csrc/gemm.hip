@@ -1666,8 +1666,9 @@ static bool stream_fits(int M, int N, int K) {
   return b > kCUs / 2 && b <= kCUs;
 }
 
-// ... or on 256x192 tiles when those alone fill the GPU (the split plan for
-// the product has a single slice: QKV at 2048 tokens).
+// A bf16 Store product also runs in one pass on the two-group kernel's
+// 256x192 tiles when those alone fill the GPU (the split plan for the
+// product has a single slice: QKV at 2048 tokens).
 static bool store_pp192(int M, int N, int K) {
   if (K % 64 != 0) return false;
   const PartialPlan p = partial_plan(M, N, K, true);
