@@ -119,9 +119,12 @@ typedef struct {
  * hold that call's intermediates: RES fp32 [n][H] the residual stream, i.e.
  * the layer's output before it is rounded to dtype; XN the FFN-normed rows
  * [n][H] (dtype); QKV [n][(nq+2nkv)hd] (dtype) whose Q columns hold the normed,
- * roped queries (its K and V columns hold the projected K and V only with fp32
- * activations; with bf16 ones K and V go from the projection's split-K sums
- * straight to the cache and those columns are not written); ATTN [n][nq*hd]
+ * roped queries (its K and V columns hold the projected K and V when the
+ * projection writes whole rows: with fp32 activations, and with bf16 ones when
+ * it runs in one pass, as for 512- and 2048-token micro-batches at the 8B
+ * shapes; when a bf16 projection splits K, and on the decode path, K and V go
+ * from the split-K sums straight to the cache and those columns are not
+ * written); ATTN [n][nq*hd]
  * attention output (dtype); ACT [n][I]
  * SwiGLU output (dtype); HEAD fp32 [H] normed last row (chunk with a head);
  * PART fp32 split-K slices of the output and down projections (bf16 only). */

@@ -311,8 +311,8 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
     TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemm_skinny(xn, H, w.w_qkv.data, scales_of(w.w_qkv), n, qkv_dim, H, part,
                                                   qkv_dim, qkv_part_stride, q_parts, s));
   } else {
-    // bf16 rows straight from a one-pass kernel when its 128-row tiles fill
-    // the GPU (512-token micro-batches), else fp32 K slices
+    // bf16 rows straight from a one-pass kernel when its tiles fill the GPU
+    // (128-row tiles at 512 tokens, 256x192 at 2048), else fp32 K slices
     const bool direct = gemm_store_direct(n, qkv_dim, H, c.wformat == TLP_W_SIGN1_G128);
     if (split && !direct) {
       g.epi = Epi::Partial; g.out = part; g.ldo = qkv_dim; g.out_f32 = true;
