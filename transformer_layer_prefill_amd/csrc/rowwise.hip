@@ -298,9 +298,31 @@ hipError_t launch_qk_rope_store(Act act, bool kv16, void* qkv, int M, int qkv_ld
   return hipGetLastError();
 }
 
+// 8 weights loaded non-temporally: the LM head reads each once per call
+typedef unsigned int lm_u32x4_t __attribute__((ext_vector_type(4)));
+typedef float lm_f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load8_w(const uint16_t* p, float v[8]) {
+  const lm_u32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const lm_u32x4_t*>(p));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8_w(const float* p, float v[8]) {
+  const lm_f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const lm_f32x4_t*>(p));
+  const lm_f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const lm_f32x4_t*>(p) + 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+
 // LM head: each wavefront owns whole rows of W; a lane streams 16-byte chunks
-// of the row and the dot product ends in one wavefront reduction.  HBM-bound:
-// the weight is read exactly once.
+// of the row, four chunks' loads in flight at a time, and the dot product ends
+// in one wavefront reduction.  HBM-bound: the weight is read exactly once.
+// (The chunks are summed in ascending order, as one chunk per step would.)
 template <typename T>
 __global__ __launch_bounds__(256) void lm_head_kernel(const float* __restrict__ xn,
                                                       const T* __restrict__ W,
@@ -312,12 +334,21 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const float* __restrict__ 
   for (int r = gw; r < V; r += nw) {
     const T* wr = W + static_cast<size_t>(r) * H;
     float acc = 0.f;
-    for (int c = lane; c < chunks; c += 64) {
-      float w[8], x[8];
-      load8(wr + c * 8, w);
-      load8(xn + c * 8, x);
+    for (int c0 = lane; c0 < chunks; c0 += 4 * 64) {
+      float w[4][8], x[4][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc += w[i] * x[i];
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < chunks) {
+          load8_w(wr + c * 8, w[u]);
+          load8(xn + c * 8, x[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c0 + 64 * u < chunks)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc += w[u][i] * x[u][i];
     }
     acc = wave_sum(acc);
     if (lane == 0) logits[r] = acc;

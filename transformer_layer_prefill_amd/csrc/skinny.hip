@@ -14,11 +14,12 @@
 // written as fp32 split-K slices that the following row kernel sums (or the
 // SwiGLU finish below, for the fused gate/up weight).
 //
-// One activation row (a decode step): its address is the same for every lane,
-// so each 128-wide chunk of it is fetched with scalar loads (read-only, through
-// the constant address space) instead of one 16-byte vector load per k-step,
-// and each lane selects its 8 columns.  Every lane then holds real activations
-// (only output column 0 is stored; other columns of the product are discarded).
+// One activation row (a decode step) with 1-bit weights: its address is the
+// same for every lane, so each 128-wide chunk of it is fetched with scalar
+// loads (read-only, through the constant address space) instead of one 16-byte
+// vector load per k-step, and each lane selects its 8 columns.  Every lane then
+// holds real activations (only output column 0 is stored; other columns of the
+// product are discarded).
 //
 // Several activation rows (2..32): the four wavefronts of a block take four
 // consecutive 32-row weight groups of the same K slice, so they share the
@@ -31,6 +32,19 @@
 // group scale of each 128-wide K chunk (16 + 2 bytes instead of 256) and
 // expands the 8 bits of each k-step into bf16 +-scale in registers; slices
 // are whole 128-wide groups.
+//
+// One activation row with dense weights takes a kernel of its own (below):
+// plain dot products on the vector ALUs, with loads that read whole 128-byte
+// lines.
+//
+// The one-row kernel reads each weight line once, in one instruction, so its
+// weight loads are non-temporal: they stream past the caches instead of
+// evicting what the other kernels of the step (the KV cache, the activations,
+// the split-K slices) still use (gate/up at the 8B decode shape 43 -> 39 µs).
+// The MFMA kernel's loads are ordinary: each of its instructions reads a
+// quarter (1-bit: an eighth) of each line it touches and the following
+// instructions read the rest from cache; non-temporal loads there refetch the
+// line from HBM (the 16-row LM head of the verify tail went from 203 to 315 µs).
 #include "common.h"
 #include "launch.h"
 
@@ -56,6 +70,11 @@ __device__ __forceinline__ bf16x8_t zero16() { return __builtin_bit_cast(bf16x8_
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const u32x4_t const_u32x4;
+
+// 16 bytes of weights, loaded non-temporally (the one-row kernel)
+__device__ __forceinline__ uint4 ldw16(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(static_cast<const u32x4_t*>(p)));
+}
 
 // activation rows: one row through scalar loads, or 2..32 rows shared by the
 // block through LDS (the K tails past the last 128-wide chunk load per lane)
@@ -231,6 +250,100 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   }
 }
 
+// One activation row, dense weights: a dot product per weight row on the
+// vector ALUs (v_dot2 multiplies bf16 pairs and adds them into fp32).  Lane
+// (r = lane / 8, c = lane % 8) reads bytes 16c .. 16c+15 of a 64-wide K
+// segment of row r of each of the wavefront's four 8-row sets, so one load
+// instruction covers 8 rows x 128 contiguous bytes (the MFMA fragment layout
+// above covers 32 rows x 32 bytes per instruction, which streams from HBM
+// more slowly: gate/up at the 8B decode shape 46 -> 43 µs with this layout).
+// Each lane keeps the activations of its 8 columns and one partial sum per row
+// set; the 8 lanes of a row add theirs at the end.  B segments of K form one
+// batch of loads, and the next batch is in flight while one is summed.  Work
+// items, K slices and outputs are those of gemm_skinny_kernel.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot8(const uint4 w, const uint4 x, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), acc, false);
+  return acc;
+}
+
+template <int B>
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(SkinnyArgs g) {
+  constexpr int SEG = 64;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= g.groups * g.splits) return;   // whole wavefronts
+  const int split = item % g.splits, grp = item / g.splits;
+  const int rr = lane >> 3, c = lane & 7;
+  const uint16_t* W = static_cast<const uint16_t*>(g.W);
+  const uint16_t* wrow[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int n = grp * 32 + 8 * q + rr;
+    wrow[q] = W + static_cast<size_t>(n < g.N ? n : g.N - 1) * g.K + 8 * c;
+  }
+  const uint16_t* xrow = g.A + 8 * c;
+  const int k_begin = split * g.k_split;
+  const int k_end = min(g.K, k_begin + g.k_split);
+
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  uint4 wa[B][4], xa[B], wb[B][4], xb[B];
+  auto load = [&](uint4 (&w)[B][4], uint4 (&x)[B], int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < B; ++s) x[s] = *reinterpret_cast<const uint4*>(xrow + k + SEG * s);
+#pragma unroll
+    for (int s = 0; s < B; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[s][q] = ldw16(wrow[q] + k + SEG * s);
+  };
+  auto sum = [&](const uint4 (&w)[B][4], const uint4 (&x)[B]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < B; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = dot8(w[s][q], x[s], acc[q]);
+  };
+  constexpr int KB = B * SEG;
+  int k = k_begin;
+  if (k + KB <= k_end) {
+    load(wa, xa, k);
+    k += KB;
+    for (;;) {
+      if (k + KB > k_end) { sum(wa, xa); break; }
+      load(wb, xb, k);
+      k += KB;
+      sum(wa, xa);
+      if (k + KB > k_end) { sum(wb, xb); break; }
+      load(wa, xa, k);
+      k += KB;
+      sum(wb, xb);
+    }
+  }
+  // remaining segments; columns past the slice's end (K % 64 != 0) read as zeros
+  for (; k < k_end; k += SEG) {
+    const bool ok = k + 8 * c < k_end;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const uint4 x = ok ? *reinterpret_cast<const uint4*>(xrow + k) : z;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = dot8(ok ? ldw16(wrow[q] + k) : z, x, acc[q]);
+  }
+  // the 8 lanes of a row hold its partial sums over disjoint columns
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int off = 4; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off, 8);
+  // lane c < 4 of row r stores row set c: weight row grp*32 + 8c + r (an
+  // empty slice stores zeros)
+  float v = acc[0];
+#pragma unroll
+  for (int q = 1; q < 4; ++q) v = c == q ? acc[q] : v;
+  const int n = grp * 32 + 8 * c + rr;
+  if (c < 4 && n < g.N) g.out[split * g.part_stride + n] = v;
+}
+
 int skinny_splits(int N, int K, bool sign1) {
   const int groups = (N + 31) / 32;
   // ~8 wavefronts per CU; 1-bit weights have 16x fewer bytes per wavefront in
@@ -271,7 +384,7 @@ hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, const void*
   const unsigned blocks = (waves + 3) / 4;
   if (M == 1) {
     if (sign1) gemm_skinny_kernel<true, kRowsOne><<<blocks, 256, 0, s>>>(g);
-    else gemm_skinny_kernel<false, kRowsOne><<<blocks, 256, 0, s>>>(g);
+    else gemv_bf16_kernel<2><<<blocks, 256, 0, s>>>(g);
   } else {
     const unsigned sblocks = static_cast<unsigned>((g.groups + 3) / 4 * splits);
     if (sign1) gemm_skinny_kernel<true, kRowsShared><<<sblocks, 256, 0, s>>>(g);
