@@ -26,7 +26,10 @@
 // activations: each 128-wide chunk of the rows is loaded once per block (one
 // 16-byte piece per thread and 16 rows) into a double-buffered LDS tile, rows
 // padded to 272 bytes so the 16 rows a read touches hit distinct banks, with
-// one barrier per chunk.
+// one barrier per chunk.  Their dense weights are loaded as whole lines (8
+// rows x 128 bytes per load instruction) and rewritten into MFMA fragments
+// through a private LDS tile per wavefront (one 16-byte write and one read per
+// lane and k-step), bit-identical to loading the fragments directly.
 //
 // 1-bit weights: lane (row r, half h) loads the row's 128 sign bits and fp16
 // group scale of each 128-wide K chunk (16 + 2 bytes instead of 256) and
@@ -37,14 +40,15 @@
 // plain dot products on the vector ALUs, with loads that read whole 128-byte
 // lines.
 //
-// The one-row kernel reads each weight line once, in one instruction, so its
-// weight loads are non-temporal: they stream past the caches instead of
-// evicting what the other kernels of the step (the KV cache, the activations,
-// the split-K slices) still use (gate/up at the 8B decode shape 43 -> 39 µs).
-// The MFMA kernel's loads are ordinary: each of its instructions reads a
-// quarter (1-bit: an eighth) of each line it touches and the following
-// instructions read the rest from cache; non-temporal loads there refetch the
-// line from HBM (the 16-row LM head of the verify tail went from 203 to 315 µs).
+// Whole-line weight loads (the one-row kernel, and dense weights with shared
+// rows) read each line once, in one instruction, so they are non-temporal:
+// they stream past the caches instead of evicting what the other kernels of
+// the step (the KV cache, the activations, the split-K slices) still use
+// (gate/up at the 8B decode shape 43 -> 39 µs).  The fragment-layout loads
+// (1-bit weights, K tails) stay ordinary: each of their instructions reads a
+// part of each line it touches and the following instructions read the rest
+// from cache, which a non-temporal load does not keep (with non-temporal
+// fragment loads the 16-row LM head of the verify tail went from 203 to 315 µs).
 #include "common.h"
 #include "launch.h"
 
@@ -86,6 +90,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   constexpr bool SHARED = ROWS == kRowsShared;   // else one row (kRowsOne)
   constexpr int AST = 17;    // LDS row stride of the shared activations, in 16-byte pieces
   __shared__ uint4 alds[SHARED ? 2 * 32 * AST : 1];
+  // dense weights with shared rows: each wavefront's 32 rows x 128 of K pass
+  // through a private 8 KB LDS tile (whole-line loads in, MFMA fragments out)
+  constexpr bool LINES = SHARED && !SIGN1;
+  __shared__ uint4 wlds[LINES ? 4 * 32 * 16 : 1];
   const int lane = threadIdx.x & 63;
   // wavefront-uniform (readfirstlane lets the compiler see it): K ranges and
   // the one-row activation addresses are scalar
@@ -109,6 +117,20 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   const uint16_t* wrow = static_cast<const uint16_t*>(g.W) + nr * g.K + 8 * lh;
   const uint32_t* brow = static_cast<const uint32_t*>(g.W) + nr * (g.K >> 5);   // 1-bit
   const uint16_t* srow = g.Wscale + nr * (g.K >> 7);                              // 1-bit
+  // whole-line loads (LINES): lane (rr, c8) loads 16 bytes at column 8*c8 of
+  // each 64-wide half of the chunk, of rows rr, rr+8, rr+16, rr+24 of the group
+  const int rr = lane >> 3, c8 = lane & 7;
+  const uint16_t* lrow[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int nq = grp * 32 + 8 * q + rr;
+    lrow[q] = static_cast<const uint16_t*>(g.W) + static_cast<size_t>(nq < g.N ? nq : g.N - 1) * g.K + 8 * c8;
+  }
+  // LDS tile: row r's 16-byte piece p at r*256 + (p ^ lsw(r))*16; the swizzle
+  // keeps the 16 lanes of each write (two rows, 8 pieces) and of each fragment
+  // read (16 rows, one piece) on distinct bank quads
+  auto lsw = [](int r) { return ((r & 1) << 3) | ((r >> 1) & 7); };
+  char* wtile = reinterpret_cast<char*>(wlds) + (LINES ? wave * 8192 : 0);
   const bool a_ok = lr < g.M;
   const uint16_t* arow = g.A + static_cast<size_t>(a_ok ? lr : 0) * g.lda + 8 * lh;
   const int k_begin = split * g.k_split;
@@ -129,9 +151,33 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
     if constexpr (SIGN1) {
       wv[0] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(brow + (k >> 5)));
       wv[1] = __builtin_bit_cast(bf16x8_t, make_uint4(srow[k >> 7], 0, 0, 0));
+    } else if constexpr (LINES) {
+      // wv[2q + h]: row rr + 8q, columns k + 64h + 8*c8 .. +8 (non-temporal:
+      // whole lines, each read once)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) wv[2 * q + h] = __builtin_bit_cast(bf16x8_t, ldw16(lrow[q] + k + 64 * h));
     } else {
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) wv[j] = ld16(wrow + k + 16 * j);
+    }
+  };
+  // LINES: rewrite the chunk as MFMA fragments (wv[j] = row lr, columns
+  // 16j + 8*lh .. +8) through this wavefront's tile; a wavefront's LDS
+  // accesses run in order, so the next chunk's writes cannot pass these reads
+  auto relayout = [&](bf16x8_t (&wv)[STEPS]) __attribute__((always_inline)) {
+    if constexpr (LINES) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = 8 * q + rr;
+          *reinterpret_cast<bf16x8_t*>(wtile + r * 256 + (((8 * h + c8) ^ lsw(r)) << 4)) = wv[2 * q + h];
+        }
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j)
+        wv[j] = *reinterpret_cast<const bf16x8_t*>(wtile + lr * 256 + (((2 * j + lh) ^ lsw(lr)) << 4));
     }
   };
   // (activations first: a wait for them leaves the weight loads in flight)
@@ -199,15 +245,17 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
     load(w0, a0, k);
     k += KB;
     for (;;) {
-      if (k + KB > k_end) { share(a0, 0); mma(w0, a0); break; }
+      if (k + KB > k_end) { share(a0, 0); relayout(w0); mma(w0, a0); break; }
       load(w1, a1, k);
       k += KB;
       share(a0, 0);
+      relayout(w0);
       mma(w0, a0);
-      if (k + KB > k_end) { share(a1, 1); mma(w1, a1); break; }
+      if (k + KB > k_end) { share(a1, 1); relayout(w1); mma(w1, a1); break; }
       load(w0, a0, k);
       k += KB;
       share(a1, 1);
+      relayout(w1);
       mma(w1, a1);
     }
   }
