@@ -117,6 +117,14 @@ SMALL = [
            n_tokens=450, start=3, max_seq=512),
     _small("bf16-qkv-stream64-ragged", hidden=512, inter=512, nq=32, nkv=16, head_dim=64,
            n_tokens=300, start=5, max_seq=320),
+    # a history of more than twice the batch over few keys (18 key blocks):
+    # the two-key-group attention form instead of key ranges; 240 blocks,
+    # ragged last 32-token slice
+    _small("bf16-ksplit-history", hidden=256, inter=512, nq=32, nkv=8, head_dim=128,
+           n_tokens=450, start=700, max_seq=1200),
+    # the same batch over 34 key blocks: key ranges (5) and their merge pass
+    _small("bf16-kvsplit-history", hidden=256, inter=512, nq=32, nkv=8, head_dim=128,
+           n_tokens=450, start=1700, max_seq=2200),
 ]
 
 

@@ -670,6 +670,11 @@ int attention_kv_splits(int M, int kv_len, int nq, int nkv) {
   if (g.waves != 4 || g.blocks >= 256) return 1;   // the grid already fills the GPU
   if (kv_len < 2 * M) return 1;   // keys mostly on the causal diagonal: ranges unbalanced
   const int nkb = (kv_len + 63) / 64;
+  // The two-key-group form keeps its partial results in LDS; while the keys
+  // are few it beats the ranges and their merge pass through memory (Llama-3
+  // shape, 512 tokens from position 512: 24 against 33 µs; from 1536: 39
+  // against 43; from 3584 the ranges win, 59 against 70).
+  if (g.hpb % 2 == 0 && 2 * g.blocks >= 192 && 2 * g.blocks <= 256 && nkb <= 32) return 1;
   int ns = (512 + g.blocks - 1) / g.blocks;        // about 512 blocks in all
   if (ns > kAttnMaxSplits) ns = kAttnMaxSplits;
   if (ns > nkb / 4) ns = nkb / 4;                  // at least 4 key blocks per range
