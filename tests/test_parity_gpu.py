@@ -227,6 +227,10 @@ DECODE = [
     _small("decode-g4-32rows-raggedK", n_tokens=32, start=1500, max_seq=1600),
     _small("decode-g8-hd64-ragged", hidden=512, inter=776, nq=16, nkv=2, head_dim=64,
            n_tokens=9, start=700, max_seq=720),
+    # one row with K and N ragged against the one-row kernel's 64-wide
+    # segments and 32-row groups (hidden 264, intermediate 1000)
+    _small("decode-one-row-ragged", hidden=264, inter=1000, nq=4, nkv=2, head_dim=64,
+           n_tokens=1, start=300, max_seq=320),
 ]
 
 # Split-KV key ranges that begin inside a wavefront's 32 query rows: the rows
