@@ -545,6 +545,54 @@ __global__ __launch_bounds__(256) void attn_combine_block_kernel(
   }
 }
 
+// Merge of at most kCombineRegRanges key ranges for many (query row, head)
+// pairs (prefill micro-batches over long histories): half a wavefront per
+// pair, HD / 32 head dims per lane.  Every lane reads the few (max, weight
+// sum) pairs itself (the half-wavefront's addresses coincide), so the merge
+// needs no cross-lane reduction: with M the largest running max,
+// o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), summed over s in order.
+constexpr int kCombineRegRanges = 8;
+template <int HD>
+__global__ __launch_bounds__(256) void attn_combine_reg_kernel(const float* __restrict__ po,
+                                                              const float* __restrict__ pml,
+                                                              int n_split, int M, int nq,
+                                                              uint16_t* __restrict__ out, int out_ld) {
+  constexpr int DPL = HD / 32;   // head dims per lane (4 or 2)
+  typedef float fv __attribute__((ext_vector_type(DPL)));
+  const int pair = blockIdx.x * 8 + (threadIdx.x >> 5);   // (row, head), head fastest
+  if (pair >= M * nq) return;                             // whole half-wavefronts
+  const int l32 = threadIdx.x & 31;
+  const size_t row = static_cast<size_t>(pair);
+  const size_t sstride = static_cast<size_t>(M) * nq;
+  float ms[kCombineRegRanges], ls[kCombineRegRanges];
+  float m = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kCombineRegRanges; ++sp)
+    if (sp < n_split) {
+      const float2 v = *reinterpret_cast<const float2*>(pml + (sp * sstride + row) * 2);
+      ms[sp] = v.x;
+      ls[sp] = v.y;
+      m = fmaxf(m, v.x);
+    }
+  float l = 0.f;
+  fv acc = {};
+#pragma unroll
+  for (int sp = 0; sp < kCombineRegRanges; ++sp)
+    if (sp < n_split) {
+      const float w = fast_exp2(ms[sp] - m);
+      l += ls[sp] * w;
+      acc += *reinterpret_cast<const fv*>(po + (sp * sstride + row) * HD + l32 * DPL) * w;
+    }
+  const float inv = 1.0f / l;
+  uint16_t* dst = out + static_cast<size_t>(pair / nq) * out_ld + (pair % nq) * HD + l32 * DPL;
+  if constexpr (DPL == 4) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                                pack_bf16x2(acc[2] * inv, acc[3] * inv));
+  } else {
+    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  }
+}
+
 // Merge of the split-KV partial results for many (query row, head) pairs
 // (prefill micro-batches): one wavefront per pair, four per block.  With M the largest running max,
 // o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  Lanes take key ranges
@@ -741,6 +789,12 @@ hipError_t launch_attention(Act act, bool kv16, const void* q, int q_ld, const v
         attn_combine_block_kernel<128><<<pairs, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
       else
         attn_combine_block_kernel<64><<<pairs, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+    } else if (ns <= kCombineRegRanges) {   // few ranges: half a wavefront per pair
+      const int cblocks = (pairs + 7) / 8;
+      if (head_dim == 128)
+        attn_combine_reg_kernel<128><<<cblocks, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
+      else
+        attn_combine_reg_kernel<64><<<cblocks, 256, 0, s>>>(a.po, a.pml, ns, M, nq, a.out, out_ld);
     } else {
       const int cblocks = (pairs + 3) / 4;
       if (head_dim == 128)
