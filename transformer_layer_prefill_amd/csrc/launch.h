@@ -70,6 +70,8 @@ bool gemm_store_direct(int M, int N, int K, bool sign1);
 // == 0): K is cut into `splits` slices and slice s writes its fp32 product
 // A W^T to out + s * part_stride (row stride ldo); every slice is written, also
 // an empty one (zeros).  skinny_splits picks the slice count for an N x K weight.
+// (One row with dense weights runs on the vector ALUs, more rows or 1-bit
+// weights on MFMAs; the slices are the same.)
 constexpr int kSkinnyMaxM = 32;
 constexpr int kSkinnyMaxSplits = 8;
 int skinny_splits(int N, int K, bool sign1);
