@@ -172,6 +172,10 @@ def split_kv_boundary_in_window(M, start, nq, nkv):
     if waves != 4 or blocks >= 256 or kv_len < 2 * M:
         return False
     nkb = -(-kv_len // 64)
+    # the two-key-group form takes over while the keys are few and its grid
+    # (twice the blocks) fills the GPU
+    if hpb % 2 == 0 and 192 <= 2 * blocks <= 256 and nkb <= 32:
+        return False
     ns = min(-(-512 // blocks), 64, nkb // 4)
     if ns < 2:
         return False
