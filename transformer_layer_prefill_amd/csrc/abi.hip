@@ -291,13 +291,20 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   // no slices to add need no fp32 copy yet: widening bf16 is exact, so the
   // FFN norm pass reads the same rows itself and writes the stream then.
   const bool defer_res = split && !x_in_f32 && in_parts == 0;
+  // One row with dense weights: the QKV projection normalises the row itself
+  // when there is nothing else for this pass to do (a bf16 row, no slices)
+  const bool one_row = skinny && n == 1 && c.wformat != TLP_W_SIGN1_G128;
+  const int q_splits1 = one_row ? skinny_splits(qkv_dim, H, false) : 0;
+  const bool fuse_norm = one_row && defer_res && gemv_norm_ok(qkv_dim, H, q_splits1);
   RowArgs r{};
-  r.x = x_in; r.x_f32 = x_in_f32; r.ldx = H;
-  r.part = part; r.n_part = in_parts; r.part_stride = part_stride;
-  r.res_out = defer_res ? nullptr : res;
-  r.gain = w.attn_norm; r.norm_out = xn;
-  r.rows = n; r.H = H; r.eps = c.rms_eps;
-  TLP_LAUNCH(TLP_K_ATTN_NORM, launch_rownorm(act, r, s));
+  if (!fuse_norm) {
+    r.x = x_in; r.x_f32 = x_in_f32; r.ldx = H;
+    r.part = part; r.n_part = in_parts; r.part_stride = part_stride;
+    r.res_out = defer_res ? nullptr : res;
+    r.gain = w.attn_norm; r.norm_out = xn;
+    r.rows = n; r.H = H; r.eps = c.rms_eps;
+    TLP_LAUNCH(TLP_K_ATTN_NORM, launch_rownorm(act, r, s));
+  }
   // 2. fused QKV projection
   GemmCall g{};
   g.act = act;
@@ -306,7 +313,11 @@ tlp_status run_layer(const tlp_config& c, const tlp_layer_weights& w, int layer,
   g.M = n; g.N = qkv_dim; g.K = H;
   int q_parts = 0;
   const size_t qkv_part_stride = static_cast<size_t>(n) * qkv_dim;
-  if (skinny) {
+  if (fuse_norm) {
+    q_parts = q_splits1;
+    TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemv_norm(x_in, w.attn_norm, c.rms_eps, w.w_qkv.data, qkv_dim, H,
+                                                part, qkv_part_stride, q_parts, s));
+  } else if (skinny) {
     q_parts = skinny_splits(qkv_dim, H, c.wformat == TLP_W_SIGN1_G128);
     TLP_LAUNCH(TLP_K_QKV_GEMM, launch_gemm_skinny(xn, H, w.w_qkv.data, scales_of(w.w_qkv), n, qkv_dim, H, part,
                                                   qkv_dim, qkv_part_stride, q_parts, s));

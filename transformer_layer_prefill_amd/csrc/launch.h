@@ -78,6 +78,16 @@ int skinny_splits(int N, int K, bool sign1);
 hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, const void* Wscale, int M,
                               int N, int K, float* out, int ldo, size_t part_stride, int splits,
                               hipStream_t s);
+// One bf16 row A [K] as stored, dense weights, normalised inside the
+// projection: the input is RMSNorm(A) * gain (gain [K], eps), by the row
+// pass's formula (only the order of the sum of squares differs) rounded to
+// bf16, so no separate norm pass is needed.
+// Slices and outputs are those of launch_gemm_skinny with M = 1.
+// gemv_norm_ok says whether a shape's K slices are short enough to be staged
+// in LDS.
+bool gemv_norm_ok(int N, int K, int splits);
+hipError_t launch_gemv_norm(const void* A, const void* gain, float eps, const void* W, int N, int K,
+                            float* out, size_t part_stride, int splits, hipStream_t s);
 // act[m][i] (bf16) = silu(g) * u with g, u the sums over `splits` fp32 slices of
 // the [M][2I] gate/up product (gate columns [0, I), up columns [I, 2I)).
 hipError_t launch_swiglu_finish(const float* part, int splits, size_t part_stride, int M, int I,

@@ -64,6 +64,9 @@ struct SkinnyArgs {
   int M, N, K;
   int splits, k_split;   // k_split: a multiple of 64
   int groups;            // ceil(N / 32)
+  // one-row kernel normalising its input row itself (launch_gemv_norm)
+  const uint16_t* gain;  // RMSNorm gain [K]
+  float eps;
 };
 
 __device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) {
@@ -308,8 +311,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
 // Each lane keeps the activations of its 8 columns and one partial sum per row
 // set; the 8 lanes of a row add theirs at the end.  B segments of K form one
 // batch of loads, and the next batch is in flight while one is summed.  Work
-// items, K slices and outputs are those of gemm_skinny_kernel.
+// items, K slices and outputs are those of gemm_skinny_kernel.  With a
+// normalised input (kGemvNorm: a decode step's QKV projection) each
+// wavefront first reduces the whole row itself and writes its K slice of
+// RMSNorm(row) * gain into LDS, so the step needs no separate norm pass.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// input of the one-row kernel: the row as stored, or RMSNorm(row) * gain
+enum GemvIn { kGemvRow = 0, kGemvNorm = 1 };
+constexpr int kGemvMaxSlice = 4096;   // longest K slice a normalised input stages in LDS
 
 __device__ __forceinline__ float dot8(const uint4 w, const uint4 x, float acc) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), acc, false);
@@ -319,11 +329,14 @@ __device__ __forceinline__ float dot8(const uint4 w, const uint4 x, float acc) {
   return acc;
 }
 
-template <int B>
+template <int B, int IN>
 __global__ __launch_bounds__(256) void gemv_bf16_kernel(SkinnyArgs g) {
   constexpr int SEG = 64;
+  // normalised input: this wavefront's K slice of the row, built in LDS
+  __shared__ uint4 xlds[IN == kGemvRow ? 1 : 4 * kGemvMaxSlice / 8];
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * 4 + wave;
   if (item >= g.groups * g.splits) return;   // whole wavefronts
   const int split = item % g.splits, grp = item / g.splits;
   const int rr = lane >> 3, c = lane & 7;
@@ -334,19 +347,67 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(SkinnyArgs g) {
     const int n = grp * 32 + 8 * q + rr;
     wrow[q] = W + static_cast<size_t>(n < g.N ? n : g.N - 1) * g.K + 8 * c;
   }
-  const uint16_t* xrow = g.A + 8 * c;
   const int k_begin = split * g.k_split;
   const int k_end = min(g.K, k_begin + g.k_split);
+  // the input row from memory (kGemvRow) or from this wavefront's LDS slice
+  // (indexed from k_begin); either way lane c reads columns 8c .. 8c+7 of a segment
+  const uint16_t* xrow = g.A + 8 * c;
+  uint16_t* const xw = reinterpret_cast<uint16_t*>(xlds) + (IN == kGemvRow ? 0 : wave * kGemvMaxSlice);
+  auto xload = [&](int k) __attribute__((always_inline)) -> uint4 {
+    if constexpr (IN == kGemvRow) return *reinterpret_cast<const uint4*>(xrow + k);
+    else return *reinterpret_cast<const uint4*>(xw + (k - k_begin) + 8 * c);
+  };
+  // (the first batch's weight loads are issued before this, so the weight
+  // stream starts with the kernel)
+  auto prologue = [&]() __attribute__((always_inline)) {
+    if constexpr (IN == kGemvNorm) {
+      // RMSNorm of the whole row, then gain * (x * inv) rounded as the row pass does
+      float ss = 0.f;
+#pragma unroll 8
+      for (int k = 8 * lane; k < g.K; k += 512) {
+        const uint4 u = *reinterpret_cast<const uint4*>(g.A + k);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = __uint_as_float(w4[i] << 16), hi = __uint_as_float(w4[i] & 0xffff0000u);
+          ss += lo * lo + hi * hi;
+        }
+      }
+      ss = wave_sum(ss);
+      const float inv = rsqrtf(ss / static_cast<float>(g.K) + g.eps);
+#pragma unroll 4
+      for (int k = k_begin + 8 * lane; k < k_end; k += 512) {
+        const uint4 u = *reinterpret_cast<const uint4*>(g.A + k);
+        const uint4 gg = *reinterpret_cast<const uint4*>(g.gain + k);
+        const uint32_t xv[4] = {u.x, u.y, u.z, u.w}, gv[4] = {gg.x, gg.y, gg.z, gg.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = __uint_as_float(xv[i] << 16), x1 = __uint_as_float(xv[i] & 0xffff0000u);
+          const float g0 = __uint_as_float(gv[i] << 16), g1 = __uint_as_float(gv[i] & 0xffff0000u);
+          o[i] = pack_bf16x2(g0 * (x0 * inv), g1 * (x1 * inv));
+        }
+        *reinterpret_cast<uint4*>(xw + (k - k_begin)) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    // (a wavefront's LDS accesses run in order: its reads below see these writes)
+  };
 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   uint4 wa[B][4], xa[B], wb[B][4], xb[B];
-  auto load = [&](uint4 (&w)[B][4], uint4 (&x)[B], int k) __attribute__((always_inline)) {
+  auto load_x = [&](uint4 (&x)[B], int k) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < B; ++s) x[s] = *reinterpret_cast<const uint4*>(xrow + k + SEG * s);
+    for (int s = 0; s < B; ++s) x[s] = xload(k + SEG * s);
+  };
+  auto load_w = [&](uint4 (&w)[B][4], int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < B; ++s)
 #pragma unroll
       for (int q = 0; q < 4; ++q) w[s][q] = ldw16(wrow[q] + k + SEG * s);
+  };
+  auto load = [&](uint4 (&w)[B][4], uint4 (&x)[B], int k) __attribute__((always_inline)) {
+    load_x(x, k);
+    load_w(w, k);
   };
   auto sum = [&](const uint4 (&w)[B][4], const uint4 (&x)[B]) __attribute__((always_inline)) {
 #pragma unroll
@@ -356,8 +417,11 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(SkinnyArgs g) {
   };
   constexpr int KB = B * SEG;
   int k = k_begin;
-  if (k + KB <= k_end) {
-    load(wa, xa, k);
+  const bool batches = k + KB <= k_end;
+  if (batches) load_w(wa, k);
+  if constexpr (IN != kGemvRow) prologue();
+  if (batches) {
+    load_x(xa, k);
     k += KB;
     for (;;) {
       if (k + KB > k_end) { sum(wa, xa); break; }
@@ -374,7 +438,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(SkinnyArgs g) {
   for (; k < k_end; k += SEG) {
     const bool ok = k + 8 * c < k_end;
     const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint4 x = ok ? *reinterpret_cast<const uint4*>(xrow + k) : z;
+    const uint4 x = ok ? xload(k) : z;
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = dot8(ok ? ldw16(wrow[q] + k) : z, x, acc[q]);
   }
@@ -390,6 +454,13 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(SkinnyArgs g) {
   for (int q = 1; q < 4; ++q) v = c == q ? acc[q] : v;
   const int n = grp * 32 + 8 * c + rr;
   if (c < 4 && n < g.N) g.out[split * g.part_stride + n] = v;
+}
+
+// K slice length of a split into `splits` slices: whole 256-wide main-loop
+// iterations when K allows (the last slice may be shorter, or empty)
+static int skinny_k_split(int K, int splits, bool sign1) {
+  const int gran = K >= 256 * splits ? 256 : (sign1 ? 128 : 64);
+  return ((K + splits - 1) / splits + gran - 1) / gran * gran;
 }
 
 int skinny_splits(int N, int K, bool sign1) {
@@ -425,19 +496,44 @@ hipError_t launch_gemm_skinny(const void* A, int lda, const void* W, const void*
   g.splits = splits;
   // slices of whole 256-wide main-loop iterations when K allows (the last
   // slice may be shorter, or empty: it then writes zeros)
-  const int gran = K >= 256 * splits ? 256 : (sign1 ? 128 : 64);
-  g.k_split = ((K + splits - 1) / splits + gran - 1) / gran * gran;
+  g.k_split = skinny_k_split(K, splits, sign1);
   g.groups = (N + 31) / 32;
   const int waves = g.groups * splits;
   const unsigned blocks = (waves + 3) / 4;
   if (M == 1) {
     if (sign1) gemm_skinny_kernel<true, kRowsOne><<<blocks, 256, 0, s>>>(g);
-    else gemv_bf16_kernel<2><<<blocks, 256, 0, s>>>(g);
+    else gemv_bf16_kernel<2, kGemvRow><<<blocks, 256, 0, s>>>(g);
   } else {
     const unsigned sblocks = static_cast<unsigned>((g.groups + 3) / 4 * splits);
     if (sign1) gemm_skinny_kernel<true, kRowsShared><<<sblocks, 256, 0, s>>>(g);
     else gemm_skinny_kernel<false, kRowsShared><<<sblocks, 256, 0, s>>>(g);
   }
+  return hipGetLastError();
+}
+
+bool gemv_norm_ok(int N, int K, int splits) {
+  return N > 0 && K > 0 && K % 8 == 0 && splits >= 1 && skinny_k_split(K, splits, false) <= kGemvMaxSlice;
+}
+
+hipError_t launch_gemv_norm(const void* A, const void* gain, float eps, const void* W, int N, int K,
+                            float* out, size_t part_stride, int splits, hipStream_t s) {
+  if (!gemv_norm_ok(N, K, splits)) return hipErrorInvalidValue;
+  SkinnyArgs g{};
+  g.A = static_cast<const uint16_t*>(A);
+  g.W = W;
+  g.out = out;
+  g.part_stride = part_stride;
+  g.lda = K;
+  g.ldo = N;
+  g.M = 1;
+  g.N = N;
+  g.K = K;
+  g.splits = splits;
+  g.k_split = skinny_k_split(K, splits, false);
+  g.groups = (N + 31) / 32;
+  g.gain = static_cast<const uint16_t*>(gain);
+  g.eps = eps;
+  gemv_bf16_kernel<2, kGemvNorm><<<(g.groups * splits + 3) / 4, 256, 0, s>>>(g);
   return hipGetLastError();
 }
 
