@@ -265,6 +265,8 @@ KV16 = [
            n_tokens=1990, start=0, max_seq=2048, kv="f16"),
     _small("kv16-decode-split", hidden=256, inter=512, nq=4, nkv=2, n_tokens=3, start=900,
            max_seq=1024, kv="f16"),
+    # one row: the QKV GEMV normalises the row itself; fp16 cache, split-KV
+    _small("kv16-one-row", n_tokens=1, start=700, max_seq=768, kv="f16"),
     _small("kv16-sign1-qknorm", hidden=512, inter=1024, nq=4, nkv=2, n_tokens=200, start=300,
            max_seq=512, qk_norm=True, eps=1e-6, wformat="sign1", kv="f16"),
 ]
