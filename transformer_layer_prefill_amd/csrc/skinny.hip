@@ -8,9 +8,11 @@
 //
 // Every wavefront multiplies 32 weight rows by all M activation rows,
 // zero-padded to the 32 columns of v_mfma_f32_32x32x16_bf16, over one slice
-// of K.  The weight rows stream from HBM straight into registers: lane
-// (row r, half h) loads the 16-byte chunks 2s + h of the row's 128-byte
-// lines, so the two lanes of a row consume whole lines.  The products are
+// of K.  In the fragment layout (1-bit weights, K tails) the weight rows
+// stream from HBM straight into registers: lane (row r, half h) loads the
+// 16-byte chunks 2s + h of the row's 128-byte lines, so the two lanes of a
+// row consume whole lines over four instructions (dense weights are loaded
+// as whole lines per instruction, below).  The products are
 // written as fp32 split-K slices that the following row kernel sums (or the
 // SwiGLU finish below, for the fused gate/up weight).
 //
@@ -38,7 +40,8 @@
 //
 // One activation row with dense weights takes a kernel of its own (below):
 // plain dot products on the vector ALUs, with loads that read whole 128-byte
-// lines.
+// lines; as the QKV projection of a decode step it also computes the
+// attention norm of its row itself.
 //
 // Whole-line weight loads (the one-row kernel, and dense weights with shared
 // rows) read each line once, in one instruction, so they are non-temporal:
